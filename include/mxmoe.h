@@ -1,0 +1,166 @@
+/*
+ * mxmoe.h -- C ABI of the MXFP8 MoE routed-expert hot path on gfx950.
+ *
+ * What the library computes
+ * -------------------------
+ * Dynamic MXFP8 quantization followed by a block-scaled grouped GEMM for the
+ * routed experts of a Mixture-of-Experts layer, forward, dgrad and wgrad:
+ *   - "MXFP8 training for MoEs" article, section "Is MXFP8 Training for MoEs
+ *     Actually Stable?": activations and weights are quantized dynamically to
+ *     MXFP8, a scaled grouped GEMM runs, the result comes back in the original
+ *     precision; section "Why Does MXFP8 Speed Up MoE Training So Much?":
+ *     the backward pass mirrors the forward.
+ *   - "MXFP8 (Micro-scaling FP8)" page, section "Definition": one shared
+ *     power-of-two scale per small block of values; section "Low-precision
+ *     Flash Attention (MXFP8 on FA4)": scales are generated along each GEMM's
+ *     K dimension, scale factors come from bit manipulation rather than
+ *     log2/round/clamp, and 32x32 square blocks (one scale per tile) make the
+ *     quantization transpose-invariant.
+ *   - "feat(moe): add MoK MXFP8 expert support" PR, review of the
+ *     mxfp8_weights argument: every expert weight exists in two quantized
+ *     orientations (weight_fp8/weight_scale for the forward, weight_t_fp8/
+ *     weight_t_scale for the backward), and a mismatched call raises.  Its
+ *     summary: unsupported settings are rejected with a clear error.
+ *
+ * Encoding (shared by every entry point)
+ * --------------------------------------
+ *   block    32 consecutive values along the contraction axis (1x32 rowwise,
+ *            32x1 colwise) or a 32x32 tile;
+ *   scale    one E8M0 byte per block: byte = clamp(floor(log2 amax) - 8,
+ *            -127, 127) + 127 (8 is E4M3's largest exponent); 0x00 for an
+ *            all-zero block; 0xFF when the block holds NaN or Inf;
+ *   element  FP8 E4M3 (bias 7, largest finite 448, 0x7F = NaN) of
+ *            value * 2^(127 - byte), rounded to nearest even, saturated to
+ *            +-448, subnormals kept, sign kept on values that round to zero;
+ *            every element of a NaN/Inf block is 0x7F.
+ *   value    decode(q) * 2^(byte - 127).
+ * bf16 is passed as uint16_t bit patterns, E4M3 and E8M0 as uint8_t.  All
+ * tensors are dense and row-major unless a leading dimension says otherwise.
+ *
+ * Memory, streams, errors
+ * -----------------------
+ *   - Every tensor pointer is a DEVICE pointer (hipMalloc'd or a torch CUDA
+ *     tensor), 16-byte aligned.  The caller owns all memory, including the
+ *     workspace of the bf16 GEMM entry points; the library never allocates,
+ *     frees or synchronizes.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call only enqueues kernels on it and returns.
+ *   - Inputs are read-only.  Outputs are overwritten in full (an expert with
+ *     no tokens gets an all-zero weight gradient).
+ *   - Host-checkable misuse (null pointers, negative or misaligned sizes, a
+ *     too-small workspace) returns a status != MX_OK before anything is
+ *     launched; mx_last_error() then describes it (thread-local text).
+ *   - Group offsets live on the device and are not checked against the host.
+ *     Preconditions: non-decreasing, offs[E-1] == M, and for wgrad every
+ *     group start a multiple of 32.  Kernels clamp offsets into [0, M], so a
+ *     violation never reads or writes out of bounds; the values are then
+ *     unspecified.
+ *   - No global state besides the error text: calls are reentrant.
+ */
+#ifndef MXMOE_H
+#define MXMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mx_status {
+  MX_OK = 0,
+  MX_ERR_NULL = 1,       /* a required pointer is NULL                        */
+  MX_ERR_SHAPE = 2,      /* a size is negative or violates a divisibility rule */
+  MX_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned                   */
+  MX_ERR_WORKSPACE = 4,  /* workspace smaller than mx_grouped_mm_workspace_bytes */
+  MX_ERR_HIP = 5         /* a kernel launch failed (text has the HIP error)    */
+} mx_status;
+
+/* Text describing the last non-OK status returned on this thread. */
+const char* mx_last_error(void);
+
+/* Library version string. */
+const char* mx_version(void);
+
+/* ------------------------------------------------------------------------
+ * Quantizers.  x is bf16 [batch, rows, cols] (batch >= 1, rows, cols >= 0).
+ * ------------------------------------------------------------------------ */
+
+/* 1x32 blocks along cols (the contraction axis of the GEMM that consumes
+ * the result).  Requires cols % 32 == 0.
+ * Out: q [batch, rows, cols] E4M3, s [batch, rows, cols/32] E8M0. */
+mx_status mx_quantize_rowwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                              uint8_t* q, uint8_t* s, void* stream);
+
+/* 32x1 blocks along rows, stored transposed so the block axis is contiguous
+ * (the 3D colwise weight quantization of the dgrad path, and the token-axis
+ * quantization of wgrad).  Requires rows % 32 == 0 and cols % 8 == 0.
+ * Out: q_t [batch, cols, rows] E4M3, s_t [batch, cols, rows/32] E8M0. */
+mx_status mx_quantize_colwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                              uint8_t* q_t, uint8_t* s_t, void* stream);
+
+/* 32x32 square blocks, elements stay in place.  Requires rows % 32 == 0 and
+ * cols % 32 == 0.  Out: q [batch, rows, cols], s [batch, rows/32, cols/32]. */
+mx_status mx_quantize_32x32(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                            uint8_t* q, uint8_t* s, void* stream);
+
+/* ------------------------------------------------------------------------
+ * The block-scaled grouped GEMM on prequantized operands.
+ *
+ *   C[i, j] = sum_k X[i, k] * Y[j, k] * 2^(sX[i, k/32] + sY[j, k/32] - 254)
+ *
+ * accumulated in fp32, stored as bf16 (round to nearest even).
+ *   mode 0: groups over the rows i of X.  X [I, Kc], sX [I, Kc/32];
+ *           Y [E, J, Kc], sY [E, J, Kc/32] (expert e's slice for group e);
+ *           C [I, J].  Rows of an empty group do not exist.
+ *   mode 1: groups over the contraction index k (weight gradient).
+ *           X [I, Kc], Y [J, Kc] (token axis contiguous), C [E, I, J];
+ *           expert e sums k in [offs[e-1], offs[e]); an empty group gives
+ *           C[e] = 0.  Group starts must be multiples of 32.
+ * offs: int32 [E] cumulative END offsets on the device (offs[-1] = 0),
+ * over rows of X (mode 0) or over k (mode 1).
+ * Requires Kc % 128 == 0, J % 8 == 0, E >= 1.
+ * Operand mapping: forward X = q(A), Y = q(W) (rowwise along K); dgrad
+ * X = q(dOut) (rowwise along N), Y = q_t(W) (colwise along N, [E, K, N]);
+ * wgrad X = q_t(dOut) [N, M], Y = q_t(A) [K, M] (colwise along tokens).
+ * ------------------------------------------------------------------------ */
+mx_status mx_grouped_gemm_mx(const uint8_t* X, const uint8_t* sX, const uint8_t* Y, const uint8_t* sY,
+                             const int32_t* offs, int mode, int64_t I, int64_t J, int64_t Kc, int64_t E,
+                             uint16_t* C, void* stream);
+
+/* ------------------------------------------------------------------------
+ * The grouped GEMMs on bf16 inputs: quantize both operands into the caller's
+ * workspace, then run the GEMM above.  M = total rows of A / dOut, grouped by
+ * offs (int32 [E] cumulative END offsets on the device).
+ * ------------------------------------------------------------------------ */
+#define MX_OP_FWD 0
+#define MX_OP_DGRAD 1
+#define MX_OP_WGRAD 2
+
+/* Bytes of workspace the bf16 entry point `op` needs (0 on invalid sizes). */
+size_t mx_grouped_mm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int64_t E);
+
+/* out [M, N] = A [M, K] @ W[e] [N, K]^T per group.  Requires K % 32 == 0,
+ * N % 8 == 0. */
+mx_status mx_grouped_mm_fwd(const uint16_t* A, const uint16_t* W, const int32_t* offs,
+                            int64_t M, int64_t N, int64_t K, int64_t E, uint16_t* out,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* dA [M, K] = dOut [M, N] @ W[e] [N, K] per group; W is quantized in 32-blocks
+ * along N.  Requires N % 32 == 0, K % 8 == 0. */
+mx_status mx_grouped_mm_dgrad(const uint16_t* dOut, const uint16_t* W, const int32_t* offs,
+                              int64_t M, int64_t N, int64_t K, int64_t E, uint16_t* dA,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* dW [E, N, K], dW[e] = dOut[g_e]^T @ A[g_e]; both operands quantized in
+ * 32-blocks along tokens.  Requires M % 32 == 0, every group start a multiple
+ * of 32 (pad groups with zero rows), N % 8 == 0, K % 8 == 0. */
+mx_status mx_grouped_mm_wgrad(const uint16_t* dOut, const uint16_t* A, const int32_t* offs,
+                              int64_t M, int64_t N, int64_t K, int64_t E, uint16_t* dW,
+                              void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXMOE_H */

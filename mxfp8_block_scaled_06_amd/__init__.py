@@ -1,0 +1,257 @@
+"""MXFP8 quantization + block-scaled grouped GEMM for MoE routed experts (gfx950).
+
+Thin Python binding of the C ABI in include/mxmoe.h.  Every function
+marshals torch tensors (device memory and the current stream) into the C
+call; all arithmetic runs in the HIP kernels of libmxmoe.so.  If the library
+has not been built, every entry point raises: there is no CPU fallback.
+
+Build:  python -m mxfp8_block_scaled_06_amd.build
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "MXError", "library_path", "load_library", "version",
+    "mx_quantize_rowwise", "mx_quantize_colwise", "mx_quantize_32x32",
+    "mx_grouped_gemm_mx", "mx_grouped_mm_workspace_bytes",
+    "mx_grouped_mm_fwd", "mx_grouped_mm_dgrad", "mx_grouped_mm_wgrad",
+    "OP_FWD", "OP_DGRAD", "OP_WGRAD",
+]
+
+OP_FWD, OP_DGRAD, OP_WGRAD = 0, 1, 2
+_STATUS = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN", 4: "MX_ERR_WORKSPACE",
+           5: "MX_ERR_HIP"}
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+class MXError(RuntimeError):
+    """A C-ABI call returned a status other than MX_OK."""
+
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: {_STATUS.get(status, status)}: {text}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "libmxmoe.so")
+
+
+def load_library():
+    """Load libmxmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m mxfp8_block_scaled_06_amd.build`")
+    lib = ctypes.CDLL(path)
+    c_i64, c_vp, c_int, c_sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.mx_last_error.restype = ctypes.c_char_p
+    lib.mx_version.restype = ctypes.c_char_p
+    for name in ("mx_quantize_rowwise", "mx_quantize_colwise", "mx_quantize_32x32"):
+        f = getattr(lib, name)
+        f.restype = c_int
+        f.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp]
+    lib.mx_grouped_gemm_mx.restype = c_int
+    lib.mx_grouped_gemm_mx.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp]
+    lib.mx_grouped_mm_workspace_bytes.restype = c_sz
+    lib.mx_grouped_mm_workspace_bytes.argtypes = [c_int, c_i64, c_i64, c_i64, c_i64]
+    for name in ("mx_grouped_mm_fwd", "mx_grouped_mm_dgrad", "mx_grouped_mm_wgrad"):
+        f = getattr(lib, name)
+        f.restype = c_int
+        f.argtypes = [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]
+    _lib = lib
+    return lib
+
+
+def version() -> str:
+    return load_library().mx_version().decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MXError(fn, status, load_library().mx_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the library has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _as3d(x):
+    if x.dim() == 2:
+        return 1, x.shape[0], x.shape[1]
+    if x.dim() == 3:
+        return x.shape[0], x.shape[1], x.shape[2]
+    raise ValueError("expected a 2-D or 3-D tensor")
+
+
+# ---------------------------------------------------------------------------
+# Quantizers
+# ---------------------------------------------------------------------------
+def mx_quantize_rowwise(x, q=None, s=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """1x32 blocks along the last axis.  x bf16 [..., R, C] -> (q uint8 same shape, s uint8 [..., R, C/32])."""
+    import torch
+    lib = load_library()
+    _require(x, torch.bfloat16, "x")
+    B, R, C = _as3d(x)
+    lead = x.shape[:-1]
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((*lead, C // 32 if C % 32 == 0 else 0), dtype=torch.uint8, device=x.device)
+    _check("mx_quantize_rowwise", lib.mx_quantize_rowwise(_ptr(x), B, R, C, _ptr(q), _ptr(s), _stream(x.device)))
+    return q, s
+
+
+def mx_quantize_colwise(x, q_t=None, s_t=None):
+    """32x1 blocks along rows, output transposed.  x bf16 [B?, R, C] ->
+    (q_t uint8 [B?, C, R], s_t uint8 [B?, C, R/32])."""
+    import torch
+    lib = load_library()
+    _require(x, torch.bfloat16, "x")
+    B, R, C = _as3d(x)
+    lead = x.shape[:-2]
+    if q_t is None:
+        q_t = torch.empty((*lead, C, R), dtype=torch.uint8, device=x.device)
+    if s_t is None:
+        s_t = torch.empty((*lead, C, R // 32 if R % 32 == 0 else 0), dtype=torch.uint8, device=x.device)
+    _check("mx_quantize_colwise",
+           lib.mx_quantize_colwise(_ptr(x), B, R, C, _ptr(q_t), _ptr(s_t), _stream(x.device)))
+    return q_t, s_t
+
+
+def mx_quantize_32x32(x, q=None, s=None):
+    """32x32 blocks.  x bf16 [B?, R, C] -> (q uint8 same shape, s uint8 [B?, R/32, C/32])."""
+    import torch
+    lib = load_library()
+    _require(x, torch.bfloat16, "x")
+    B, R, C = _as3d(x)
+    lead = x.shape[:-2]
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((*lead, R // 32, C // 32), dtype=torch.uint8, device=x.device)
+    _check("mx_quantize_32x32", lib.mx_quantize_32x32(_ptr(x), B, R, C, _ptr(q), _ptr(s), _stream(x.device)))
+    return q, s
+
+
+# ---------------------------------------------------------------------------
+# Grouped GEMM on prequantized operands
+# ---------------------------------------------------------------------------
+def mx_grouped_gemm_mx(X, sX, Y, sY, offs, mode: int, out=None):
+    """C[i,j] = sum_k X[i,k] Y[j,k] 2^(sX+sY-254).  mode 0: Y [E,J,Kc], C [I,J];
+    mode 1 (groups over k): Y [J,Kc], C [E,I,J].  Returns C (bf16)."""
+    import torch
+    lib = load_library()
+    for t, n in ((X, "X"), (sX, "sX"), (Y, "Y"), (sY, "sY")):
+        _require(t, torch.uint8, n)
+    _require(offs, torch.int32, "offs")
+    E = offs.shape[0]
+    I, Kc = X.shape
+    J = Y.shape[1] if mode == 0 else Y.shape[0]
+    if out is None:
+        shape = (I, J) if mode == 0 else (E, I, J)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=X.device)
+    _check("mx_grouped_gemm_mx",
+           lib.mx_grouped_gemm_mx(_ptr(X), _ptr(sX), _ptr(Y), _ptr(sY), _ptr(offs), mode, I, J, Kc, E,
+                                  _ptr(out), _stream(X.device)))
+    return out
+
+
+def mx_grouped_mm_workspace_bytes(op: int, M: int, N: int, K: int, E: int) -> int:
+    return int(load_library().mx_grouped_mm_workspace_bytes(op, M, N, K, E))
+
+
+def _ws(op, M, N, K, E, device, ws):
+    import torch
+    need = mx_grouped_mm_workspace_bytes(op, M, N, K, E)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return ws
+
+
+# ---------------------------------------------------------------------------
+# Grouped GEMMs on bf16 inputs (quantize both operands, then GEMM)
+# ---------------------------------------------------------------------------
+def mx_grouped_mm_fwd(A, W, offs, out=None, ws=None):
+    """out [M, N] = A [M, K] @ W[e] [N, K]^T per expert group (offs: int32 END offsets)."""
+    import torch
+    lib = load_library()
+    _require(A, torch.bfloat16, "A")
+    _require(W, torch.bfloat16, "W")
+    _require(offs, torch.int32, "offs")
+    M, K = A.shape
+    E, N, K2 = W.shape
+    if K2 != K:
+        raise ValueError(f"A has K={K} but W has K={K2}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    ws = _ws(OP_FWD, M, N, K, E, A.device, ws)
+    _check("mx_grouped_mm_fwd",
+           lib.mx_grouped_mm_fwd(_ptr(A), _ptr(W), _ptr(offs), M, N, K, E, _ptr(out), _ptr(ws), ws.numel(),
+                                 _stream(A.device)))
+    return out
+
+
+def mx_grouped_mm_dgrad(dOut, W, offs, out=None, ws=None):
+    """dA [M, K] = dOut [M, N] @ W[e] [N, K] per expert group."""
+    import torch
+    lib = load_library()
+    _require(dOut, torch.bfloat16, "dOut")
+    _require(W, torch.bfloat16, "W")
+    _require(offs, torch.int32, "offs")
+    M, N = dOut.shape
+    E, N2, K = W.shape
+    if N2 != N:
+        raise ValueError(f"dOut has N={N} but W has N={N2}")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=dOut.device)
+    ws = _ws(OP_DGRAD, M, N, K, E, dOut.device, ws)
+    _check("mx_grouped_mm_dgrad",
+           lib.mx_grouped_mm_dgrad(_ptr(dOut), _ptr(W), _ptr(offs), M, N, K, E, _ptr(out), _ptr(ws), ws.numel(),
+                                   _stream(dOut.device)))
+    return out
+
+
+def mx_grouped_mm_wgrad(dOut, A, offs, out=None, ws=None):
+    """dW [E, N, K], dW[e] = dOut[g_e]^T @ A[g_e] (groups padded to multiples of 32)."""
+    import torch
+    lib = load_library()
+    _require(dOut, torch.bfloat16, "dOut")
+    _require(A, torch.bfloat16, "A")
+    _require(offs, torch.int32, "offs")
+    M, N = dOut.shape
+    M2, K = A.shape
+    if M2 != M:
+        raise ValueError(f"dOut has M={M} but A has M={M2}")
+    E = offs.shape[0]
+    if out is None:
+        out = torch.empty((E, N, K), dtype=torch.bfloat16, device=A.device)
+    ws = _ws(OP_WGRAD, M, N, K, E, A.device, ws)
+    _check("mx_grouped_mm_wgrad",
+           lib.mx_grouped_mm_wgrad(_ptr(dOut), _ptr(A), _ptr(offs), M, N, K, E, _ptr(out), _ptr(ws), ws.numel(),
+                                   _stream(A.device)))
+    return out

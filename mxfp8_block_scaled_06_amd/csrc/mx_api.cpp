@@ -1,0 +1,267 @@
+// C ABI of the MXFP8 MoE hot path (declared in include/mxmoe.h).
+//
+// Host-side only: argument validation with a clear error on every
+// unsupported setting (the "feat(moe): add MoK MXFP8 expert support" PR
+// rejects unsupported configurations with a clear error and raises on a
+// mismatched weight/precision contract), workspace carving, and kernel
+// launches on the caller's stream.  Nothing here allocates, frees or
+// synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "mx_kernels.h"
+#include "mxmoe.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mx_status fail(mx_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+mx_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MX_OK;
+  return fail(MX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// Checks shared by the quantizers.
+mx_status check_quant(const char* fn, const void* x, int64_t batch, int64_t rows, int64_t cols, const void* q,
+                      const void* s) {
+  if (batch < 1) return fail(MX_ERR_SHAPE, "%s: batch must be >= 1 (got %lld)", fn, (long long)batch);
+  if (rows < 0 || cols < 0) return fail(MX_ERR_SHAPE, "%s: negative size rows=%lld cols=%lld", fn, (long long)rows,
+                                        (long long)cols);
+  if (rows == 0 || cols == 0) return MX_OK;
+  if (!x || !q || !s) return fail(MX_ERR_NULL, "%s: null pointer (x=%p q=%p s=%p)", fn, x, q, s);
+  if (!aligned(x, 16) || !aligned(q, 16))
+    return fail(MX_ERR_ALIGN, "%s: x and q must be 16-byte aligned (x=%p q=%p)", fn, x, q);
+  return MX_OK;
+}
+
+struct WsLayout {
+  size_t off[4];
+  size_t total;
+};
+
+// Workspace regions: [X codes, X scales, Y codes, Y scales], 256-byte aligned.
+WsLayout ws_layout(int op, int64_t M, int64_t N, int64_t K, int64_t E) {
+  WsLayout L{};
+  size_t sz[4];
+  if (op == MX_OP_FWD) {
+    sz[0] = (size_t)M * K;
+    sz[1] = (size_t)M * (K / 32);
+    sz[2] = (size_t)E * N * K;
+    sz[3] = (size_t)E * N * (K / 32);
+  } else if (op == MX_OP_DGRAD) {
+    sz[0] = (size_t)M * N;
+    sz[1] = (size_t)M * (N / 32);
+    sz[2] = (size_t)E * K * N;
+    sz[3] = (size_t)E * K * (N / 32);
+  } else {
+    const int64_t Mp = round_up(M, 128);
+    sz[0] = (size_t)N * Mp;
+    sz[1] = (size_t)N * (Mp / 32);
+    sz[2] = (size_t)K * Mp;
+    sz[3] = (size_t)K * (Mp / 32);
+  }
+  size_t o = 0;
+  for (int i = 0; i < 4; ++i) {
+    L.off[i] = o;
+    o = align_up(o + sz[i], 256);
+  }
+  L.total = o;
+  return L;
+}
+
+mx_status check_mm(const char* fn, const void* a, const void* b, const void* offs, const void* out, int64_t M,
+                   int64_t N, int64_t K, int64_t E) {
+  if (M < 0 || N < 0 || K < 0) return fail(MX_ERR_SHAPE, "%s: negative size M=%lld N=%lld K=%lld", fn,
+                                           (long long)M, (long long)N, (long long)K);
+  if (E < 1 || E > mxk::kMaxExperts)
+    return fail(MX_ERR_SHAPE, "%s: number of experts E=%lld outside [1, %d]", fn, (long long)E, mxk::kMaxExperts);
+  if (!a || !b || !offs || !out) return fail(MX_ERR_NULL, "%s: null pointer", fn);
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(out, 16) || !aligned(offs, 4))
+    return fail(MX_ERR_ALIGN, "%s: tensors must be 16-byte aligned", fn);
+  return MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mx_last_error(void) { return g_last_error.c_str(); }
+
+const char* mx_version(void) { return "mxmoe 0.1.0 (gfx950)"; }
+
+mx_status mx_quantize_rowwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s,
+                              void* stream) {
+  mx_status st = check_quant("mx_quantize_rowwise", x, batch, rows, cols, q, s);
+  if (st != MX_OK) return st;
+  if (cols % 32 != 0) return fail(MX_ERR_SHAPE, "mx_quantize_rowwise: cols=%lld is not a multiple of 32",
+                                  (long long)cols);
+  if (rows == 0 || cols == 0) return MX_OK;
+  return hip_status(mxk::launch_quant_rowwise(x, batch * rows, cols, q, s, (hipStream_t)stream),
+                    "mx_quantize_rowwise launch");
+}
+
+mx_status mx_quantize_colwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q_t,
+                              uint8_t* s_t, void* stream) {
+  mx_status st = check_quant("mx_quantize_colwise", x, batch, rows, cols, q_t, s_t);
+  if (st != MX_OK) return st;
+  if (rows % 32 != 0) return fail(MX_ERR_SHAPE, "mx_quantize_colwise: rows=%lld is not a multiple of 32",
+                                  (long long)rows);
+  if (cols % 8 != 0) return fail(MX_ERR_SHAPE, "mx_quantize_colwise: cols=%lld is not a multiple of 8",
+                                 (long long)cols);
+  if (rows == 0 || cols == 0) return MX_OK;
+  if ((rows + 127) / 128 > 65535 || batch > 65535)
+    return fail(MX_ERR_SHAPE, "mx_quantize_colwise: rows or batch too large for one launch");
+  return hip_status(
+      mxk::launch_quant_colwise(x, batch, rows, cols, q_t, rows, s_t, rows / 32, (hipStream_t)stream),
+      "mx_quantize_colwise launch");
+}
+
+mx_status mx_quantize_32x32(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s,
+                            void* stream) {
+  mx_status st = check_quant("mx_quantize_32x32", x, batch, rows, cols, q, s);
+  if (st != MX_OK) return st;
+  if (rows % 32 != 0 || cols % 32 != 0)
+    return fail(MX_ERR_SHAPE, "mx_quantize_32x32: rows=%lld and cols=%lld must be multiples of 32",
+                (long long)rows, (long long)cols);
+  if (rows == 0 || cols == 0) return MX_OK;
+  if (batch * rows / 32 > 65535) return fail(MX_ERR_SHAPE, "mx_quantize_32x32: too many row blocks for one launch");
+  return hip_status(mxk::launch_quant_32x32(x, batch * rows, cols, q, s, (hipStream_t)stream),
+                    "mx_quantize_32x32 launch");
+}
+
+mx_status mx_grouped_gemm_mx(const uint8_t* X, const uint8_t* sX, const uint8_t* Y, const uint8_t* sY,
+                             const int32_t* offs, int mode, int64_t I, int64_t J, int64_t Kc, int64_t E, uint16_t* C,
+                             void* stream) {
+  const char* fn = "mx_grouped_gemm_mx";
+  if (mode != 0 && mode != 1) return fail(MX_ERR_SHAPE, "%s: mode must be 0 or 1 (got %d)", fn, mode);
+  if (I < 0 || J < 0 || Kc < 0) return fail(MX_ERR_SHAPE, "%s: negative size", fn);
+  if (E < 1 || E > mxk::kMaxExperts)
+    return fail(MX_ERR_SHAPE, "%s: number of experts E=%lld outside [1, %d]", fn, (long long)E, mxk::kMaxExperts);
+  if (Kc % 128 != 0) return fail(MX_ERR_SHAPE, "%s: Kc=%lld is not a multiple of 128", fn, (long long)Kc);
+  if (J % 8 != 0) return fail(MX_ERR_SHAPE, "%s: J=%lld is not a multiple of 8", fn, (long long)J);
+  const bool empty_out = (mode == 0) ? (I == 0 || J == 0) : (I == 0 || J == 0);
+  if (empty_out) return MX_OK;
+  if (!C || !offs) return fail(MX_ERR_NULL, "%s: null output or offsets", fn);
+  if (Kc > 0 && (!X || !sX || !Y || !sY)) return fail(MX_ERR_NULL, "%s: null operand", fn);
+  if (!aligned(X, 16) || !aligned(Y, 16) || !aligned(C, 16) || !aligned(sX, 4) || !aligned(sY, 4) ||
+      !aligned(offs, 4))
+    return fail(MX_ERR_ALIGN, "%s: X, Y, C must be 16-byte and scales/offsets 4-byte aligned", fn);
+  mxk::GemmArgs a{};
+  a.X = X;
+  a.sX = sX;
+  a.Y = Y;
+  a.sY = sY;
+  a.offs = offs;
+  a.C = C;
+  a.I = I;
+  a.J = J;
+  a.Kc = Kc;
+  a.E = (int)E;
+  a.mode = mode;
+  a.ldx = Kc;
+  a.ldsx = Kc / 32;
+  a.ldy = Kc;
+  a.ldsy = Kc / 32;
+  a.y_estride = J * Kc;
+  a.sy_estride = J * (Kc / 32);
+  a.sx_total = I * (Kc / 32);
+  a.sy_total_per_e = J * (Kc / 32);
+  a.ldc = J;
+  a.c_estride = I * J;
+  return hip_status(mxk::launch_grouped_gemm(a, (hipStream_t)stream), "mx_grouped_gemm_mx launch");
+}
+
+size_t mx_grouped_mm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int64_t E) {
+  if (op < MX_OP_FWD || op > MX_OP_WGRAD || M < 0 || N < 0 || K < 0 || E < 1) return 0;
+  return ws_layout(op, M, N, K, E).total;
+}
+
+mx_status mx_grouped_mm_fwd(const uint16_t* A, const uint16_t* W, const int32_t* offs, int64_t M, int64_t N,
+                            int64_t K, int64_t E, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "mx_grouped_mm_fwd";
+  mx_status st = check_mm(fn, A, W, offs, out, M, N, K, E);
+  if (st != MX_OK) return st;
+  if (K % 128 != 0) return fail(MX_ERR_SHAPE, "%s: K=%lld is not a multiple of 128", fn, (long long)K);
+  if (N % 8 != 0) return fail(MX_ERR_SHAPE, "%s: N=%lld is not a multiple of 8", fn, (long long)N);
+  const WsLayout L = ws_layout(MX_OP_FWD, M, N, K, E);
+  if (!ws || ws_bytes < L.total)
+    return fail(MX_ERR_WORKSPACE, "%s: workspace of %zu bytes at %p, need %zu", fn, ws_bytes, ws, L.total);
+  if (!aligned(ws, 256)) return fail(MX_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  if (M == 0 || N == 0) return MX_OK;
+  uint8_t* w8 = (uint8_t*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *qA = w8 + L.off[0], *sA = w8 + L.off[1], *qW = w8 + L.off[2], *sW = w8 + L.off[3];
+  if ((st = hip_status(mxk::launch_quant_rowwise(A, M, K, qA, sA, s), "fwd quantize A")) != MX_OK) return st;
+  if ((st = hip_status(mxk::launch_quant_rowwise(W, E * N, K, qW, sW, s), "fwd quantize W")) != MX_OK) return st;
+  return mx_grouped_gemm_mx(qA, sA, qW, sW, offs, 0, M, N, K, E, out, stream);
+}
+
+mx_status mx_grouped_mm_dgrad(const uint16_t* dOut, const uint16_t* W, const int32_t* offs, int64_t M, int64_t N,
+                              int64_t K, int64_t E, uint16_t* dA, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "mx_grouped_mm_dgrad";
+  mx_status st = check_mm(fn, dOut, W, offs, dA, M, N, K, E);
+  if (st != MX_OK) return st;
+  if (N % 128 != 0) return fail(MX_ERR_SHAPE, "%s: N=%lld is not a multiple of 128", fn, (long long)N);
+  if (K % 8 != 0) return fail(MX_ERR_SHAPE, "%s: K=%lld is not a multiple of 8", fn, (long long)K);
+  const WsLayout L = ws_layout(MX_OP_DGRAD, M, N, K, E);
+  if (!ws || ws_bytes < L.total)
+    return fail(MX_ERR_WORKSPACE, "%s: workspace of %zu bytes at %p, need %zu", fn, ws_bytes, ws, L.total);
+  if (!aligned(ws, 256)) return fail(MX_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  if (M == 0 || K == 0) return MX_OK;
+  if ((N + 127) / 128 > 65535 || E > 65535) return fail(MX_ERR_SHAPE, "%s: N too large for one launch", fn);
+  uint8_t* w8 = (uint8_t*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *qG = w8 + L.off[0], *sG = w8 + L.off[1], *qWt = w8 + L.off[2], *sWt = w8 + L.off[3];
+  if ((st = hip_status(mxk::launch_quant_rowwise(dOut, M, N, qG, sG, s), "dgrad quantize dOut")) != MX_OK) return st;
+  // W [E, N, K] quantized in 32-blocks along N, stored transposed [E, K, N]
+  if ((st = hip_status(mxk::launch_quant_colwise(W, E, N, K, qWt, N, sWt, N / 32, s), "dgrad quantize W")) != MX_OK)
+    return st;
+  return mx_grouped_gemm_mx(qG, sG, qWt, sWt, offs, 0, M, K, N, E, dA, stream);
+}
+
+mx_status mx_grouped_mm_wgrad(const uint16_t* dOut, const uint16_t* A, const int32_t* offs, int64_t M, int64_t N,
+                              int64_t K, int64_t E, uint16_t* dW, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "mx_grouped_mm_wgrad";
+  mx_status st = check_mm(fn, dOut, A, offs, dW, M, N, K, E);
+  if (st != MX_OK) return st;
+  if (M % 32 != 0) return fail(MX_ERR_SHAPE, "%s: M=%lld is not a multiple of 32", fn, (long long)M);
+  if (N % 8 != 0 || K % 8 != 0)
+    return fail(MX_ERR_SHAPE, "%s: N=%lld and K=%lld must be multiples of 8", fn, (long long)N, (long long)K);
+  const WsLayout L = ws_layout(MX_OP_WGRAD, M, N, K, E);
+  if (!ws || ws_bytes < L.total)
+    return fail(MX_ERR_WORKSPACE, "%s: workspace of %zu bytes at %p, need %zu", fn, ws_bytes, ws, L.total);
+  if (!aligned(ws, 256)) return fail(MX_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  if (N == 0 || K == 0) return MX_OK;
+  if ((M + 127) / 128 > 65535) return fail(MX_ERR_SHAPE, "%s: M too large for one launch", fn);
+  const int64_t Mp = round_up(M, 128);
+  uint8_t* w8 = (uint8_t*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *qGt = w8 + L.off[0], *sGt = w8 + L.off[1], *qAt = w8 + L.off[2], *sAt = w8 + L.off[3];
+  // dOut [M, N] and A [M, K] in 32-blocks along tokens, stored [N, Mp] and [K, Mp]
+  if ((st = hip_status(mxk::launch_quant_colwise(dOut, 1, M, N, qGt, Mp, sGt, Mp / 32, s), "wgrad quantize dOut")) !=
+      MX_OK)
+    return st;
+  if ((st = hip_status(mxk::launch_quant_colwise(A, 1, M, K, qAt, Mp, sAt, Mp / 32, s), "wgrad quantize A")) != MX_OK)
+    return st;
+  return mx_grouped_gemm_mx(qGt, sGt, qAt, sAt, offs, 1, N, K, Mp, E, dW, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,206 @@
+// MXFP8 quantize kernels for gfx950: rowwise 1x32, colwise 32x1 (transposed
+// output) and 32x32 square blocks.
+//
+// Operation: "MXFP8 (Micro-scaling FP8)" page, sections "Definition" (one
+// shared power-of-two scale per small block of values) and "Low-precision
+// Flash Attention (MXFP8 on FA4)" (scales along each GEMM's K dimension,
+// derived by bit manipulation instead of log2/round/clamp; 32x32 blocks with a
+// wave-wide max-abs reduction, transpose-invariant).  The 3D colwise weight
+// quantization for the backward is the pytorch/ao "3d quant colwise scaling
+// kernel" of the PR timeline.
+//
+// Per block: amax over the |bf16| bit patterns (integer max, exact), E8M0 byte
+// = max(exponent field - 8, 0) (0xFF for NaN/Inf), every element multiplied
+// by 2^(127 - byte) in fp32 (exact: bf16 has 8 significant bits), clamped to
+// +-448 and converted to E4M3 with the hardware RNE convert.  All three are
+// HBM-bound streaming passes: 2 bytes read, 1 + 1/32 (or 1/1024) written per
+// element.
+#include "mx_device.h"
+#include "mx_kernels.h"
+
+namespace mxk {
+
+// ---------------------------------------------------------------------------
+// Rowwise: x viewed as [rows, cols] (batch folded into rows), dense outputs.
+// One 16-byte chunk (8 values) per lane and load; a DPP quad holds one block.
+// Each thread handles kRowU chunks spaced by the block size so every wave-wide
+// load instruction reads 1 KiB of contiguous input.
+// ---------------------------------------------------------------------------
+constexpr int kRowThreads = 256;
+constexpr int kRowU = 4;
+
+__global__ __launch_bounds__(kRowThreads) void quant_rowwise_kernel(const uint16_t* __restrict__ x,
+                                                                    int64_t nchunks,
+                                                                    uint8_t* __restrict__ q,
+                                                                    uint8_t* __restrict__ s) {
+  const int64_t base = (int64_t)blockIdx.x * (kRowThreads * kRowU) + threadIdx.x;
+  v4i w[kRowU];
+#pragma unroll
+  for (int u = 0; u < kRowU; ++u) {
+    const int64_t idx = base + (int64_t)u * kRowThreads;
+    if (idx < nchunks) {
+      w[u] = __builtin_nontemporal_load((const v4i*)(x + idx * 8));
+    } else {
+      w[u] = (v4i){0, 0, 0, 0};
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kRowU; ++u) {
+    const int64_t idx = base + (int64_t)u * kRowThreads;
+    // chunks 4k..4k+3 form one block; nchunks is a multiple of 4, so a quad
+    // is either fully in range or fully out of range.
+    const uint32_t am = quad_max(absmax8(w[u]));
+    if (idx < nchunks) {
+      const uint32_t byte = e8m0_from_absbits(am);
+      v2i codes;
+      if (byte == 0xFFu) {
+        codes = (v2i){0x7F7F7F7F, 0x7F7F7F7F};
+      } else {
+        codes = quant8(w[u], inv_scale_from_e8m0(byte));
+      }
+      *(v2i*)(q + idx * 8) = codes;
+      if ((threadIdx.x & 3) == 0) s[idx >> 2] = (uint8_t)byte;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Colwise: x [batch, rows, cols] -> q_t [batch, cols, ldq], s_t [batch, cols, lds]
+// (ldq >= rows, lds >= rows/32).  A workgroup stages a 128x128 bf16 tile in
+// LDS (coalesced 256-byte row segments), then wave w quantizes rows
+// [32w, 32w+32) of the tile: lane l owns columns 2l and 2l+1, reads its 32
+// dwords conflict-free (one LDS row per step), and writes two 32-byte runs of
+// the transposed output.
+// ---------------------------------------------------------------------------
+constexpr int kColTile = 128;
+
+__global__ __launch_bounds__(256) void quant_colwise_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                            int64_t cols, uint8_t* __restrict__ q_t,
+                                                            int64_t ldq, uint8_t* __restrict__ s_t,
+                                                            int64_t lds) {
+  __shared__ v4i tile[kColTile * (kColTile / 8)];  // [128 rows][16 chunks of 8 bf16]
+  const int tid = threadIdx.x;
+  const int64_t b = blockIdx.z;
+  const int64_t r0 = (int64_t)blockIdx.y * kColTile;
+  const int64_t c0 = (int64_t)blockIdx.x * kColTile;
+  const uint16_t* xb = x + b * rows * cols;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int chunk = it * 256 + tid;
+    const int rr = chunk >> 4, cc = chunk & 15;
+    const int64_t row = r0 + rr, col = c0 + cc * 8;
+    v4i w = (v4i){0, 0, 0, 0};
+    if (row < rows && col < cols) w = __builtin_nontemporal_load((const v4i*)(xb + row * cols + col));
+    tile[rr * 16 + cc] = w;
+  }
+  __syncthreads();
+  const int wv = tid >> 6, lane = tid & 63;
+  const int64_t rb = r0 + 32 * wv;     // first row of this wave's block
+  const int64_t col = c0 + 2 * lane;   // even; cols % 8 == 0 so col+1 is valid too
+  if (rb >= rows || col >= cols) return;
+  const uint32_t* t32 = (const uint32_t*)tile;
+  uint32_t v[32];
+  uint32_t am0 = 0, am1 = 0;
+#pragma unroll
+  for (int t = 0; t < 32; ++t) {
+    v[t] = t32[(32 * wv + t) * 64 + lane];
+    am0 = max(am0, v[t] & 0x7FFFu);
+    am1 = max(am1, (v[t] >> 16) & 0x7FFFu);
+  }
+  const uint32_t byte0 = e8m0_from_absbits(am0), byte1 = e8m0_from_absbits(am1);
+  const float m0 = inv_scale_from_e8m0(byte0 == 0xFFu ? 127u : byte0);
+  const float m1 = inv_scale_from_e8m0(byte1 == 0xFFu ? 127u : byte1);
+  v4i out0[2], out1[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int t = h * 16 + d * 4;
+      int a = cvt2_e4m3<false>(bf16lo(v[t]) * m0, bf16lo(v[t + 1]) * m0, 0);
+      a = cvt2_e4m3<true>(bf16lo(v[t + 2]) * m0, bf16lo(v[t + 3]) * m0, a);
+      int c = cvt2_e4m3<false>(bf16hi(v[t]) * m1, bf16hi(v[t + 1]) * m1, 0);
+      c = cvt2_e4m3<true>(bf16hi(v[t + 2]) * m1, bf16hi(v[t + 3]) * m1, c);
+      out0[h][d] = byte0 == 0xFFu ? 0x7F7F7F7F : a;
+      out1[h][d] = byte1 == 0xFFu ? 0x7F7F7F7F : c;
+    }
+  }
+  uint8_t* q0 = q_t + (b * cols + col) * ldq + rb;
+  uint8_t* q1 = q0 + ldq;
+  *(v4i*)(q0) = out0[0];
+  *(v4i*)(q0 + 16) = out0[1];
+  *(v4i*)(q1) = out1[0];
+  *(v4i*)(q1 + 16) = out1[1];
+  uint8_t* sp = s_t + (b * cols + col) * lds + (rb >> 5);
+  sp[0] = (uint8_t)byte0;
+  sp[lds] = (uint8_t)byte1;
+}
+
+// ---------------------------------------------------------------------------
+// 32x32: x viewed as [rows, cols] (batch folded into rows; rows % 32 == 0).
+// A workgroup covers 32 rows x 256 columns; wave w covers columns
+// [64w, 64w+64) = two 32x32 tiles.  Lane l holds 8 columns (chunk l%8) of rows
+// l/8 + 8u, u = 0..3.  The tile amax is a wave reduction over the 32 lanes
+// sharing bit 2 of the lane id (DPP quad max, then xor-shuffles 8/16/32).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_32x32_kernel(const uint16_t* __restrict__ x, int64_t cols,
+                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int64_t r0 = (int64_t)blockIdx.y * 32;
+  const int64_t col = (int64_t)blockIdx.x * 256 + wv * 64 + (lane & 7) * 8;
+  const bool valid = col < cols;  // cols % 32 == 0: whole tiles are valid or not
+  v4i w[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t row = r0 + (lane >> 3) + 8 * u;
+    w[u] = valid ? __builtin_nontemporal_load((const v4i*)(x + row * cols + col)) : (v4i){0, 0, 0, 0};
+  }
+  uint32_t am = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) am = max(am, absmax8(w[u]));
+  am = quad_max(am);
+  am = max(am, (uint32_t)__shfl_xor((int)am, 8));
+  am = max(am, (uint32_t)__shfl_xor((int)am, 16));
+  am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+  if (!valid) return;
+  const uint32_t byte = e8m0_from_absbits(am);
+  const float m = inv_scale_from_e8m0(byte == 0xFFu ? 127u : byte);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t row = r0 + (lane >> 3) + 8 * u;
+    v2i codes = byte == 0xFFu ? (v2i){0x7F7F7F7F, 0x7F7F7F7F} : quant8(w[u], m);
+    *(v2i*)(q + row * cols + col) = codes;
+  }
+  if ((lane & 3) == 0 && (lane >> 3) == 0) s[(r0 >> 5) * (cols >> 5) + (col >> 5)] = (uint8_t)byte;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (sizes validated by the caller).
+// ---------------------------------------------------------------------------
+hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows_total, int64_t cols, uint8_t* q, uint8_t* s,
+                                hipStream_t st) {
+  const int64_t nchunks = rows_total * (cols / 8);
+  if (nchunks == 0) return hipSuccess;
+  const int64_t per_block = (int64_t)kRowThreads * kRowU;
+  const int64_t grid = (nchunks + per_block - 1) / per_block;
+  hipLaunchKernelGGL(quant_rowwise_kernel, dim3((unsigned)grid), dim3(kRowThreads), 0, st, x, nchunks, q, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_colwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q_t,
+                                int64_t ldq, uint8_t* s_t, int64_t lds, hipStream_t st) {
+  if (batch == 0 || rows == 0 || cols == 0) return hipSuccess;
+  dim3 grid((unsigned)((cols + kColTile - 1) / kColTile), (unsigned)((rows + kColTile - 1) / kColTile),
+            (unsigned)batch);
+  hipLaunchKernelGGL(quant_colwise_kernel, grid, dim3(256), 0, st, x, rows, cols, q_t, ldq, s_t, lds);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_32x32(const uint16_t* x, int64_t rows_total, int64_t cols, uint8_t* q, uint8_t* s,
+                              hipStream_t st) {
+  if (rows_total == 0 || cols == 0) return hipSuccess;
+  dim3 grid((unsigned)((cols + 255) / 256), (unsigned)(rows_total / 32));
+  hipLaunchKernelGGL(quant_32x32_kernel, grid, dim3(256), 0, st, x, cols, q, s);
+  return hipGetLastError();
+}
+
+}  // namespace mxk

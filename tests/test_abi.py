@@ -1,0 +1,103 @@
+"""The C-ABI library loads and exports every entry point include/mxmoe.h
+declares; host-side argument validation works without a GPU (no kernel is
+launched on these paths)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp8_block_scaled_06_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxmoe.h")
+
+
+def _lib():
+    if not os.path.exists(mx.library_path()):
+        from mxfp8_block_scaled_06_amd import build
+        build.build()
+    return mx.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("mx_quantize_rowwise", "mx_quantize_colwise", "mx_quantize_32x32", "mx_grouped_mm_fwd",
+              "mx_grouped_mm_dgrad", "mx_grouped_mm_wgrad", "mx_grouped_gemm_mx",
+              "mx_grouped_mm_workspace_bytes", "mx_last_error", "mx_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for n in _declared_functions():
+        assert hasattr(lib, n), f"{n} declared in mxmoe.h but not exported"
+    assert mx.version().startswith("mxmoe")
+
+
+FAKE = 1 << 20      # a 16-byte aligned non-null address; never dereferenced on these paths
+
+
+def _err(lib):
+    return lib.mx_last_error().decode()
+
+
+def test_quantize_validation_errors():
+    lib = _lib()
+    assert lib.mx_quantize_rowwise(FAKE, 1, 4, 48, FAKE, FAKE, None) == 2
+    assert "multiple of 32" in _err(lib)
+    assert lib.mx_quantize_rowwise(FAKE, 0, 4, 64, FAKE, FAKE, None) == 2
+    assert lib.mx_quantize_rowwise(None, 1, 4, 64, FAKE, FAKE, None) == 1
+    assert lib.mx_quantize_rowwise(FAKE + 8, 1, 4, 64, FAKE, FAKE, None) == 3
+    assert lib.mx_quantize_colwise(FAKE, 1, 48, 64, FAKE, FAKE, None) == 2
+    assert lib.mx_quantize_colwise(FAKE, 1, 64, 12, FAKE, FAKE, None) == 2
+    assert lib.mx_quantize_32x32(FAKE, 1, 64, 48, FAKE, FAKE, None) == 2
+    assert lib.mx_quantize_rowwise(FAKE, 1, -1, 64, FAKE, FAKE, None) == 2
+    # empty tensors are valid and launch nothing
+    assert lib.mx_quantize_rowwise(None, 1, 0, 64, None, None, None) == 0
+
+
+def test_gemm_validation_errors():
+    lib = _lib()
+    f = lib.mx_grouped_gemm_mx
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 64, 64, 128, 1, FAKE, None) == 2       # bad mode
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 64, 96, 1, FAKE, None) == 2        # Kc % 128
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 60, 128, 1, FAKE, None) == 2       # J % 8
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 64, 128, 0, FAKE, None) == 2       # E < 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 64, 128, 5000, FAKE, None) == 2    # E too large
+    assert f(FAKE, FAKE, None, FAKE, FAKE, 0, 64, 64, 128, 1, FAKE, None) == 1       # null Y
+    assert f(FAKE, FAKE, FAKE + 4, FAKE, FAKE, 0, 64, 64, 128, 1, FAKE, None) == 3   # misaligned Y
+    g = lib.mx_grouped_mm_fwd
+    need = lib.mx_grouped_mm_workspace_bytes(0, 256, 512, 256, 2)
+    assert need >= 256 * 256 + 2 * 512 * 256
+    assert g(FAKE, FAKE, FAKE, 256, 512, 256, 2, FAKE, FAKE, need - 1, None) == 4    # workspace
+    assert "workspace" in _err(lib)
+    assert g(FAKE, FAKE, FAKE, 256, 512, 224, 2, FAKE, FAKE, 1 << 40, None) == 2     # K % 128
+    assert lib.mx_grouped_mm_wgrad(FAKE, FAKE, FAKE, 250, 64, 64, 2, FAKE, FAKE, 1 << 40, None) == 2
+    assert lib.mx_grouped_mm_dgrad(FAKE, FAKE, FAKE, 256, 96, 64, 2, FAKE, FAKE, 1 << 40, None) == 2
+    assert lib.mx_grouped_mm_workspace_bytes(7, 1, 1, 1, 1) == 0
+
+
+def test_workspace_sizes_cover_both_operands():
+    lib = _lib()
+    M, N, K, E = 16384, 8192, 5120, 16
+    fwd = lib.mx_grouped_mm_workspace_bytes(0, M, N, K, E)
+    assert fwd >= M * K * 33 // 32 + E * N * K * 33 // 32
+    wg = lib.mx_grouped_mm_workspace_bytes(2, 16416, N, K, E)
+    mp = 16512                                     # tokens padded to a multiple of 128
+    assert wg >= (N + K) * mp * 33 // 32
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    _lib()
+    with pytest.raises(ValueError, match="GPU tensor"):
+        mx.mx_quantize_rowwise(torch.zeros((4, 64), dtype=torch.bfloat16))

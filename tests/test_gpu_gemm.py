@@ -1,0 +1,237 @@
+"""GPU parity of the block-scaled grouped GEMM (forward, dgrad, wgrad and the
+GEMM on prequantized operands) against the fp64 oracle, through the C ABI.
+
+Tolerance (criterion R1, oracle/compare.py): every element must satisfy
+|g - r| <= 0.5 ulp_bf16 + 2e-3 * max(|r|, sigma/16), i.e. the 2e-3 relative
+bound for fp32 accumulation on top of the final bf16 rounding, floored at
+sigma/16 so outputs near zero are judged on the output's scale."""
+
+import numpy as np
+import pytest
+
+import oracle
+from mxfp8_block_scaled_06_amd import inputs as inp
+from gpu_util import require_gpu, to_dev_bf16, to_dev_u8, to_dev_i32, bf16_host_bits, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _r1(g_bits, ref, tag, sigma=None):
+    rep = oracle.r1_check(g_bits, ref, sigma=sigma)
+    log(f"{tag}: n={rep['n']} bad={rep['n_bad']} max_err/tol={rep['max_err_over_tol']:.3f} "
+        f"normwise={rep['normwise_rel']:.2e} exact_rne={rep['exact_rne_rate']:.3f}")
+    assert rep["ok"], f"{tag}: {rep}"
+    return rep
+
+
+def _fwd(A, W, offs):
+    import mxfp8_block_scaled_06_amd as mx
+    return bf16_host_bits(mx.mx_grouped_mm_fwd(to_dev_bf16(A), to_dev_bf16(W), to_dev_i32(offs)))
+
+
+def _dgrad(G, W, offs):
+    import mxfp8_block_scaled_06_amd as mx
+    return bf16_host_bits(mx.mx_grouped_mm_dgrad(to_dev_bf16(G), to_dev_bf16(W), to_dev_i32(offs)))
+
+
+def _wgrad(G, A, offs):
+    import mxfp8_block_scaled_06_amd as mx
+    return bf16_host_bits(mx.mx_grouped_mm_wgrad(to_dev_bf16(G), to_dev_bf16(A), to_dev_i32(offs)))
+
+
+def test_fwd_tiny_workload():
+    require_gpu()
+    x = inp.make_inputs("tiny")
+    log(f"fwd tiny counts={x.counts.tolist()}")
+    _r1(_fwd(x.A, x.W, x.offs), oracle.grouped_mm_fwd(x.A, x.W, x.offs), "fwd tiny")
+
+
+ROW_CASES = {
+    "ragged": [1, 31, 32, 33, 255, 256, 257, 100],
+    "empty_first_last": [0, 300, 0, 200, 0],
+    "consecutive_empty": [70, 0, 0, 0, 190],
+    "all_in_one": [0, 0, 513, 0],
+    "single_expert": [777],
+    "zipf_like": [600, 150, 40, 9, 3, 1, 0, 0],
+}
+
+
+@pytest.mark.parametrize("case", sorted(ROW_CASES))
+def test_fwd_group_edge_cases(case):
+    require_gpu()
+    counts = ROW_CASES[case]
+    offs = inp.offsets_from_counts(counts)
+    M, K, N, E = sum(counts), 384, 520, len(counts)
+    A = inp.random_bf16((M, K), seed=100 + len(case), outliers=True)
+    W = inp.random_bf16((E, N, K), seed=200 + len(case), std=0.02)
+    log(f"fwd case={case} counts={counts} K={K} N={N}")
+    _r1(_fwd(A, W, offs), oracle.grouped_mm_fwd(A, W, offs), f"fwd {case}")
+
+
+@pytest.mark.parametrize("case", ["ragged", "empty_first_last", "single_expert"])
+def test_dgrad_group_edge_cases(case):
+    require_gpu()
+    counts = ROW_CASES[case]
+    offs = inp.offsets_from_counts(counts)
+    M, K, N, E = sum(counts), 264, 384, len(counts)
+    G = inp.random_bf16((M, N), seed=300 + len(case), std=1e-3)
+    W = inp.random_bf16((E, N, K), seed=400 + len(case), std=0.02)
+    log(f"dgrad case={case} counts={counts} N={N} K={K}")
+    _r1(_dgrad(G, W, offs), oracle.grouped_mm_dgrad(G, W, offs), f"dgrad {case}")
+
+
+WG_CASES = {
+    "padded_mixed": [64, 0, 96, 32, 0, 160],
+    "unaligned_starts": [32, 96, 224, 32],      # group starts not multiples of 128
+    "all_empty_but_one": [0, 0, 288, 0],
+    "single": [416],
+}
+
+
+@pytest.mark.parametrize("case", sorted(WG_CASES))
+def test_wgrad_group_edge_cases(case):
+    require_gpu()
+    counts = WG_CASES[case]
+    offs = inp.offsets_from_counts(counts)
+    M, K, N, E = sum(counts), 264, 200, len(counts)
+    A = inp.random_bf16((M, K), seed=500 + len(case), outliers=True)
+    G = inp.random_bf16((M, N), seed=600 + len(case), std=1e-3)
+    log(f"wgrad case={case} counts={counts} N={N} K={K}")
+    got = _wgrad(G, A, offs)
+    ref = oracle.grouped_mm_wgrad(G, A, offs)
+    for e, c in enumerate(counts):
+        if c == 0:
+            assert (got[e] == 0).all(), f"empty expert {e} must get exact zeros"
+    _r1(got, ref, f"wgrad {case}")
+
+
+def _random_codes(rng, shape):
+    c = rng.integers(0, 256, size=shape, dtype=np.int64)
+    c = np.where((c & 0x7F) == 0x7F, c ^ 1, c)      # no NaN codes
+    return c.astype(np.uint8)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_gemm_mx_random_operands(mode):
+    """The GEMM alone, on seeded random E4M3 codes and E8M0 scales."""
+    require_gpu()
+    import mxfp8_block_scaled_06_amd as mx
+    rng = np.random.default_rng(700 + mode)
+    if mode == 0:
+        counts = [130, 0, 257, 61]
+        I, J, Kc, E = sum(counts), 296, 384, len(counts)
+        X, Y = _random_codes(rng, (I, Kc)), _random_codes(rng, (E, J, Kc))
+        sX = rng.integers(112, 142, size=(I, Kc // 32)).astype(np.uint8)
+        sY = rng.integers(112, 142, size=(E, J, Kc // 32)).astype(np.uint8)
+    else:
+        counts = [96, 32, 0, 160, 64]
+        I, J, E = 264, 200, len(counts)
+        Kc = 384                      # >= sum(counts), multiple of 128
+        X, Y = _random_codes(rng, (I, Kc)), _random_codes(rng, (J, Kc))
+        sX = rng.integers(112, 142, size=(I, Kc // 32)).astype(np.uint8)
+        sY = rng.integers(112, 142, size=(J, Kc // 32)).astype(np.uint8)
+    offs = inp.offsets_from_counts(counts)
+    log(f"gemm_mx mode={mode} counts={counts}")
+    C = mx.mx_grouped_gemm_mx(to_dev_u8(X), to_dev_u8(sX), to_dev_u8(Y), to_dev_u8(sY), to_dev_i32(offs), mode)
+    _r1(bf16_host_bits(C), oracle.grouped_gemm_mx(X, sX, Y, sY, offs, mode), f"gemm_mx mode {mode}")
+
+
+def test_gemm_deterministic_and_errors():
+    torch = require_gpu()
+    import mxfp8_block_scaled_06_amd as mx
+    x = inp.make_inputs("tiny")
+    A, W, offs = to_dev_bf16(x.A), to_dev_bf16(x.W), to_dev_i32(x.offs)
+    a = mx.mx_grouped_mm_fwd(A, W, offs)
+    b = mx.mx_grouped_mm_fwd(A, W, offs)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    with pytest.raises(mx.MXError, match="MX_ERR_SHAPE"):
+        mx.mx_grouped_mm_fwd(A[:, :224].contiguous(), W[:, :, :224].contiguous(), offs)
+    with pytest.raises(mx.MXError, match="MX_ERR_WORKSPACE"):
+        mx.mx_grouped_mm_fwd(A, W, offs, ws=torch.empty(1024, dtype=torch.uint8, device="cuda:0"))
+    with pytest.raises(mx.MXError, match="MX_ERR_SHAPE"):
+        mx.mx_grouped_mm_wgrad(to_dev_bf16(x.A[:250]), to_dev_bf16(x.A[:250]), offs)
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, sampled outputs (the bench's launch configuration).
+# ---------------------------------------------------------------------------
+_CACHE = {}
+
+
+def _inputs(name, with_grad=False):
+    key = (name, with_grad)
+    if key not in _CACHE:
+        _CACHE.clear()
+        _CACHE[key] = inp.make_inputs(name, with_grad=with_grad)
+    return _CACHE[key]
+
+
+def _sample_rows_by_expert(x, rng, n_experts=2, per_expert=6):
+    bounds = oracle.group_bounds(x.offs, x.M_rows)
+    live = [e for e, (a, b) in enumerate(bounds) if b > a]
+    chosen = rng.choice(live, size=min(n_experts, len(live)), replace=False)
+    rows = {}
+    for e in chosen:
+        a, b = bounds[e]
+        r = np.unique(np.concatenate([[a, b - 1], rng.integers(a, b, size=per_expert)]))
+        rows[int(e)] = r
+    return rows
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["llama4_fwd", "debug_shard", "deepseek_share"])
+def test_fwd_full_size_sampled(name):
+    require_gpu()
+    x = _inputs(name)
+    log(f"fwd full {name} M={x.M_rows} counts[:8]={x.counts[:8].tolist()}")
+    got = _fwd(x.A, x.W, x.offs)
+    rng = np.random.default_rng(800)
+    qA_rows = {}
+    refs, gots = [], []
+    for e, rows in _sample_rows_by_expert(x, rng).items():
+        qW, sW = oracle.quantize_rowwise(x.W[e])
+        qA, sA = oracle.quantize_rowwise(x.A[rows])
+        ref = oracle.dequant_rowwise(qA, sA) @ oracle.dequant_rowwise(qW, sW).T
+        refs.append(ref)
+        gots.append(got[rows])
+    ref = np.concatenate(refs)
+    _r1(np.concatenate(gots), ref, f"fwd full {name}")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["llama4_bwd", "debug_shard"])
+def test_dgrad_full_size_sampled(name):
+    require_gpu()
+    x = _inputs(name, with_grad=True)
+    log(f"dgrad full {name} M={x.M_rows}")
+    got = _dgrad(x.dOut, x.W, x.offs)
+    rng = np.random.default_rng(801)
+    refs, gots = [], []
+    for e, rows in _sample_rows_by_expert(x, rng).items():
+        qWt, sWt = oracle.quantize_colwise(x.W[e])          # [K, N]
+        qG, sG = oracle.quantize_rowwise(x.dOut[rows])
+        refs.append(oracle.dequant_rowwise(qG, sG) @ oracle.dequant_rowwise(qWt, sWt).T)
+        gots.append(got[rows])
+    _r1(np.concatenate(gots), np.concatenate(refs), f"dgrad full {name}")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["llama4_bwd", "debug_shard"])
+def test_wgrad_full_size_sampled(name):
+    torch = require_gpu()
+    import mxfp8_block_scaled_06_amd as mx
+    x = _inputs(name, with_grad=True)
+    log(f"wgrad full {name} M={x.M_rows}")
+    dW = mx.mx_grouped_mm_wgrad(to_dev_bf16(x.dOut), to_dev_bf16(x.A), to_dev_i32(x.offs))
+    rng = np.random.default_rng(802)
+    bounds = oracle.group_bounds(x.offs, x.M_rows)
+    live = [e for e, (a, b) in enumerate(bounds) if b > a]
+    refs, gots = [], []
+    for e in rng.choice(live, size=min(2, len(live)), replace=False):
+        a, b = bounds[int(e)]
+        n_rows = np.sort(rng.choice(x.W.shape[1] if x.W is not None else x.dOut.shape[1], size=8, replace=False))
+        qGt, sGt = oracle.quantize_colwise(np.ascontiguousarray(x.dOut[a:b][:, n_rows]))   # [8, m_e]
+        qAt, sAt = oracle.quantize_colwise(np.ascontiguousarray(x.A[a:b]))                 # [K, m_e]
+        refs.append(oracle.dequant_rowwise(qGt, sGt) @ oracle.dequant_rowwise(qAt, sAt).T)
+        gots.append(bf16_host_bits(dW[int(e)][torch.as_tensor(n_rows, device=dW.device)]))
+    _r1(np.concatenate(gots), np.concatenate(refs), f"wgrad full {name}")
