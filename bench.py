@@ -1,0 +1,304 @@
+"""Benchmark of the MXFP8 MoE routed-expert hot path on one MI355X.
+
+One step = one training pass of the routed-expert grouped GEMMs over one
+batch of routed tokens, Llama4-Scout-shaped (E=16 experts, 16384 tokens
+routed top-1 by a uniform multinomial, K=5120, N=8192, groups padded with
+zero rows to multiples of 32):
+    forward  out = A @ W[e]^T      (quantize A and W rowwise, grouped GEMM)
+    dgrad    dA  = dOut @ W[e]     (quantize dOut rowwise, W colwise, GEMM)
+    wgrad    dW  = dOut^T @ A      (quantize dOut and A along tokens, GEMM)
+each through the library's bf16 entry points, so every quantize kernel, the
+tile scheduler, the GEMM main loop and the bf16 epilogue run in the step.
+
+Printed: one JSON line.  `value` = algorithmic GEMM TFLOP/s of the whole
+step (2*M*N*K per GEMM on the real tokens, quantization time included).
+Extra fields report, measured in the same run: GEMM-only TFLOP/s per op on
+prequantized operands (HIP events around each launch), quantize GB/s on the
+[65600, 5120] sweep tensor, the roofline of the dominant kernel and the CPU
+oracle timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_MXFP8_TFLOPS = 5000.0      # MI355X dense MXFP8 MFMA, published
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
+GEMM_KERNEL = "grouped_gemm_kernel<0, false>"
+GEMM_SOURCE = os.path.join(ROOT, "mxfp8_block_scaled_06_amd", "csrc", "mx_gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fwd_llama4_traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--reps", type=int, default=10, help="launches per GEMM-only / quantize timing")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    p.add_argument("--no-quant-sweep", action="store_true")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run a plain 1 GiB device copy (HBM counter calibration for rocprofv3 --pmc)")
+    return p.parse_args()
+
+
+def dev_bf16(torch, bits, dev):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def time_launches(torch, fn, reps):
+    """Average duration (ms) of `fn` launches, HIP events on the current stream."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    ts = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return {"mean_ms": sum(ts) / len(ts), "median_ms": ts[len(ts) // 2], "min_ms": ts[0], "max_ms": ts[-1]}
+
+
+def traffic_for_current_kernel():
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None
+    if the GEMM source changed since those counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+        if rec.get("gemm_source_sha256") != src:
+            return None
+        return rec.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(x, budget_rows=96):
+    """The oracle, as it stands, on a bounded sample of the forward: one expert's
+    weights quantized and `budget_rows` of its tokens multiplied in fp64."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count()
+    bounds = oracle.group_bounds(x.offs, x.M_rows)
+    e = int(np.argmax([b - a for a, b in bounds]))
+    a, _ = bounds[e]
+    rows = np.arange(a, a + budget_rows)
+    t0 = time.perf_counter()
+    qW, sW = oracle.quantize_rowwise(x.W[e])
+    qA, sA = oracle.quantize_rowwise(x.A[rows])
+    out = oracle.dequant_rowwise(qA, sA) @ oracle.dequant_rowwise(qW, sW).T
+    dt = time.perf_counter() - t0
+    flops = 2.0 * budget_rows * x.W.shape[1] * x.W.shape[2]
+    assert out.shape == (budget_rows, x.W.shape[1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"forward of {budget_rows} tokens of expert {e} incl. quantizing that expert's "
+                      f"[{x.W.shape[1]}, {x.W.shape[2]}] weights (fp64 numpy); {dt:.1f} s",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path runs on a single MI355X "
+              f"and multi-GPU sharding is not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mxfp8_block_scaled_06_amd as mx
+    from mxfp8_block_scaled_06_amd import inputs as inp
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mx.load_library()
+    dev = torch.device("cuda:0")
+
+    # ---------------- inputs (resident in HBM before timing) ----------------
+    t0 = time.perf_counter()
+    x = inp.make_inputs("llama4_bwd", with_grad=True)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f}s: M_pad={x.M_rows} real={int(x.counts.sum())}")
+    E, N, K = x.W.shape
+    M = x.M_rows
+    m_real = int(x.counts.sum())
+    A = dev_bf16(torch, x.A, dev)
+    W = dev_bf16(torch, x.W, dev)
+    G = dev_bf16(torch, x.dOut, dev)
+    offs = torch.from_numpy(x.offs).to(dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dA = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dW = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
+    ws = {op: torch.empty(mx.mx_grouped_mm_workspace_bytes(op, M, N, K, E), dtype=torch.uint8, device=dev)
+          for op in (mx.OP_FWD, mx.OP_DGRAD, mx.OP_WGRAD)}
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        mx.mx_grouped_mm_fwd(A, W, offs, out=out, ws=ws[mx.OP_FWD])
+        if ev is not None:
+            ev[1].record()
+        mx.mx_grouped_mm_dgrad(G, W, offs, out=dA, ws=ws[mx.OP_DGRAD])
+        if ev is not None:
+            ev[2].record()
+        mx.mx_grouped_mm_wgrad(G, A, offs, out=dW, ws=ws[mx.OP_WGRAD])
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    prim_ms = {name: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+               for i, name in enumerate(("fwd", "dgrad", "wgrad"))}
+    gemm_flops_real = 3 * 2.0 * m_real * N * K
+    gemm_flops_pad = 3 * 2.0 * M * N * K
+    value = gemm_flops_real / (ms_per_step * 1e-3) / 1e12
+    log(f"step {ms_per_step:.3f} ms ({prim_ms}); wall {wall:.2f}s for {args.steps} steps")
+
+    # ---------------- GEMM only, prequantized operands ----------------
+    qA, sA = mx.mx_quantize_rowwise(A)
+    qW, sW = mx.mx_quantize_rowwise(W)
+    qG, sG = mx.mx_quantize_rowwise(G)
+    qWt, sWt = mx.mx_quantize_colwise(W)
+    # wgrad operands: the token axis is the contraction axis, padded to a
+    # multiple of 128 with zero rows (the layout the bf16 entry point uses)
+    Mp = (M + 127) // 128 * 128
+    Gp = torch.zeros((Mp, N), dtype=torch.bfloat16, device=dev)
+    Ap = torch.zeros((Mp, K), dtype=torch.bfloat16, device=dev)
+    Gp[:M] = G
+    Ap[:M] = A
+    qGt, sGt = mx.mx_quantize_colwise(Gp)
+    qAt, sAt = mx.mx_quantize_colwise(Ap)
+    del Gp, Ap
+    c_fwd = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    c_dg = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    c_wg = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
+    gemm = {}
+    cases = {
+        "fwd": (lambda: mx.mx_grouped_gemm_mx(qA, sA, qW, sW, offs, 0, out=c_fwd), 2.0 * M * N * K),
+        "dgrad": (lambda: mx.mx_grouped_gemm_mx(qG, sG, qWt, sWt, offs, 0, out=c_dg), 2.0 * M * N * K),
+        "wgrad": (lambda: mx.mx_grouped_gemm_mx(qGt, sGt, qAt, sAt, offs, 1, out=c_wg), 2.0 * M * N * K),
+    }
+    for name, (fn, flops) in cases.items():
+        fn()
+        torch.cuda.synchronize()
+        t = time_launches(torch, fn, args.reps)
+        tf = flops / (t["mean_ms"] * 1e-3) / 1e12
+        gemm[name] = {"ms": t["mean_ms"], "median_ms": t["median_ms"], "tflops": tf,
+                      "frac_of_peak": tf / PEAK_MXFP8_TFLOPS, "flops_per_launch": flops}
+        log(f"gemm-only {name}: {t['mean_ms']:.3f} ms  {tf:.1f} TFLOP/s  {100 * tf / PEAK_MXFP8_TFLOPS:.1f}% of peak")
+    del qA, sA, qW, sW, qG, sG, qWt, sWt, qGt, sGt, qAt, sAt, c_fwd, c_dg, c_wg
+
+    # dominant kernel: the rows-grouped GEMM (forward and dgrad launches, equal flops)
+    dom_ms = (gemm["fwd"]["ms"] + gemm["dgrad"]["ms"]) / 2
+    dom_flops = 2.0 * M * N * K
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MXFP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_MXFP8_TFLOPS, "traffic": traffic_for_current_kernel(),
+                "kernel": GEMM_KERNEL, "flops_per_launch": dom_flops, "avg_launch_ms": dom_ms}
+
+    # ---------------- quantize sweep ----------------
+    quant = {}
+    if not args.no_quant_sweep:
+        del out, dA, dW
+        torch.cuda.empty_cache()
+        X = dev_bf16(torch, inp.make_sweep(), dev)
+        R, C = X.shape
+        q = torch.empty((R, C), dtype=torch.uint8, device=dev)
+        s_row = torch.empty((R, C // 32), dtype=torch.uint8, device=dev)
+        qt = torch.empty((C, R), dtype=torch.uint8, device=dev)
+        s_col = torch.empty((C, R // 32), dtype=torch.uint8, device=dev)
+        s_sq = torch.empty((R // 32, C // 32), dtype=torch.uint8, device=dev)
+        for name, fn, nbytes in (
+                ("rowwise", lambda: mx.mx_quantize_rowwise(X, q, s_row), 3 * R * C + R * C // 32),
+                ("colwise", lambda: mx.mx_quantize_colwise(X, qt, s_col), 3 * R * C + R * C // 32),
+                ("32x32", lambda: mx.mx_quantize_32x32(X, q, s_sq), 3 * R * C + R * C // 1024)):
+            fn()
+            torch.cuda.synchronize()
+            t = time_launches(torch, fn, args.reps)
+            gbs = nbytes / (t["mean_ms"] * 1e-3) / 1e9
+            quant[name] = {"ms": t["mean_ms"], "GB_s": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS,
+                           "bytes": nbytes}
+            log(f"quant {name} [{R},{C}]: {t['mean_ms']:.3f} ms  {gbs:.0f} GB/s  {100 * gbs / PEAK_HBM_GBS:.1f}%")
+        del X, q, s_row, qt, s_col, s_sq
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---------------- CPU oracle leg ----------------
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(x)
+        log(f"cpu oracle: {cpu['value']:.5f} TFLOP/s on {cpu['cores']} threads ({cpu['sample']})")
+        cpu.pop("seconds", None)
+
+    rec = {
+        "metric": "MXFP8 grouped-GEMM TFLOP/s (fwd/dgrad/wgrad) and % of MX-FP8 peak; quant GB/s",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3/e8m0 (fp32 accumulate, bf16 out)",
+        "data": "synthetic (seeded N(0,1) activations with 0.1% x50 outliers, N(0,0.02) weights, "
+                "N(0,1e-3) grads)",
+        "config": {"workload": "Llama4-Scout-shaped routed experts, fwd + dgrad + wgrad: E=16, "
+                               f"{m_real} tokens (uniform top-1 routing, groups padded to 32 -> {M} rows), "
+                               "K=5120, N=8192",
+                   "E": E, "tokens": m_real, "rows_padded": M, "K": K, "N": N},
+        "frac_of_peak": value / PEAK_MXFP8_TFLOPS,
+        "step_breakdown_ms": prim_ms,
+        "step_tflops_on_padded_rows": gemm_flops_pad / (ms_per_step * 1e-3) / 1e12,
+        "gemm_only": gemm,
+        "quant_sweep_65600x5120": quant,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "gpu": torch.cuda.get_device_name(0),
+        "library": mx.version(),
+    }
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

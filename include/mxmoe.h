@@ -128,6 +128,13 @@ mx_status mx_grouped_gemm_mx(const uint8_t* X, const uint8_t* sX, const uint8_t*
                              const int32_t* offs, int mode, int64_t I, int64_t J, int64_t Kc, int64_t E,
                              uint16_t* C, void* stream);
 
+/* The same GEMM with the fp32 accumulators stored unrounded (C is float,
+ * same shapes and rules).  For callers that accumulate results in fp32, e.g.
+ * weight gradients summed over micro-batches before the optimizer step. */
+mx_status mx_grouped_gemm_mx_f32(const uint8_t* X, const uint8_t* sX, const uint8_t* Y, const uint8_t* sY,
+                                 const int32_t* offs, int mode, int64_t I, int64_t J, int64_t Kc, int64_t E,
+                                 float* C, void* stream);
+
 /* ------------------------------------------------------------------------
  * The grouped GEMMs on bf16 inputs: quantize both operands into the caller's
  * workspace, then run the GEMM above.  M = total rows of A / dOut, grouped by

@@ -17,7 +17,7 @@ from typing import Optional, Tuple
 __all__ = [
     "MXError", "library_path", "load_library", "version",
     "mx_quantize_rowwise", "mx_quantize_colwise", "mx_quantize_32x32",
-    "mx_grouped_gemm_mx", "mx_grouped_mm_workspace_bytes",
+    "mx_grouped_gemm_mx", "mx_grouped_gemm_mx_f32", "mx_grouped_mm_workspace_bytes",
     "mx_grouped_mm_fwd", "mx_grouped_mm_dgrad", "mx_grouped_mm_wgrad",
     "OP_FWD", "OP_DGRAD", "OP_WGRAD",
 ]
@@ -58,8 +58,10 @@ def load_library():
         f = getattr(lib, name)
         f.restype = c_int
         f.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp]
-    lib.mx_grouped_gemm_mx.restype = c_int
-    lib.mx_grouped_gemm_mx.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp]
+    for name in ("mx_grouped_gemm_mx", "mx_grouped_gemm_mx_f32"):
+        f = getattr(lib, name)
+        f.restype = c_int
+        f.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp]
     lib.mx_grouped_mm_workspace_bytes.restype = c_sz
     lib.mx_grouped_mm_workspace_bytes.argtypes = [c_int, c_i64, c_i64, c_i64, c_i64]
     for name in ("mx_grouped_mm_fwd", "mx_grouped_mm_dgrad", "mx_grouped_mm_wgrad"):
@@ -161,11 +163,16 @@ def mx_quantize_32x32(x, q=None, s=None):
 # ---------------------------------------------------------------------------
 # Grouped GEMM on prequantized operands
 # ---------------------------------------------------------------------------
-def mx_grouped_gemm_mx(X, sX, Y, sY, offs, mode: int, out=None):
+def mx_grouped_gemm_mx(X, sX, Y, sY, offs, mode: int, out=None, out_dtype=None):
     """C[i,j] = sum_k X[i,k] Y[j,k] 2^(sX+sY-254).  mode 0: Y [E,J,Kc], C [I,J];
-    mode 1 (groups over k): Y [J,Kc], C [E,I,J].  Returns C (bf16)."""
+    mode 1 (groups over k): Y [J,Kc], C [E,I,J].  Returns C (bf16, or fp32
+    with out_dtype=torch.float32)."""
     import torch
     lib = load_library()
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.bfloat16
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
     for t, n in ((X, "X"), (sX, "sX"), (Y, "Y"), (sY, "sY")):
         _require(t, torch.uint8, n)
     _require(offs, torch.int32, "offs")
@@ -174,11 +181,18 @@ def mx_grouped_gemm_mx(X, sX, Y, sY, offs, mode: int, out=None):
     J = Y.shape[1] if mode == 0 else Y.shape[0]
     if out is None:
         shape = (I, J) if mode == 0 else (E, I, J)
-        out = torch.empty(shape, dtype=torch.bfloat16, device=X.device)
-    _check("mx_grouped_gemm_mx",
-           lib.mx_grouped_gemm_mx(_ptr(X), _ptr(sX), _ptr(Y), _ptr(sY), _ptr(offs), mode, I, J, Kc, E,
-                                  _ptr(out), _stream(X.device)))
+        out = torch.empty(shape, dtype=out_dtype, device=X.device)
+    _require(out, out_dtype, "out")
+    name = "mx_grouped_gemm_mx" if out_dtype == torch.bfloat16 else "mx_grouped_gemm_mx_f32"
+    _check(name, getattr(lib, name)(_ptr(X), _ptr(sX), _ptr(Y), _ptr(sY), _ptr(offs), mode, I, J, Kc, E,
+                                    _ptr(out), _stream(X.device)))
     return out
+
+
+def mx_grouped_gemm_mx_f32(X, sX, Y, sY, offs, mode: int, out=None):
+    """mx_grouped_gemm_mx with fp32 output (accumulators stored unrounded)."""
+    import torch
+    return mx_grouped_gemm_mx(X, sX, Y, sY, offs, mode, out=out, out_dtype=torch.float32)
 
 
 def mx_grouped_mm_workspace_bytes(op: int, M: int, N: int, K: int, E: int) -> int:

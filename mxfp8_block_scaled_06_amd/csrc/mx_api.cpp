@@ -41,10 +41,14 @@ int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 // Checks shared by the quantizers.
 mx_status check_quant(const char* fn, const void* x, int64_t batch, int64_t rows, int64_t cols, const void* q,
-                      const void* s) {
+                      const void* s, int64_t row_mult, int64_t col_mult) {
   if (batch < 1) return fail(MX_ERR_SHAPE, "%s: batch must be >= 1 (got %lld)", fn, (long long)batch);
   if (rows < 0 || cols < 0) return fail(MX_ERR_SHAPE, "%s: negative size rows=%lld cols=%lld", fn, (long long)rows,
                                         (long long)cols);
+  if (rows % row_mult != 0)
+    return fail(MX_ERR_SHAPE, "%s: rows=%lld is not a multiple of %lld", fn, (long long)rows, (long long)row_mult);
+  if (cols % col_mult != 0)
+    return fail(MX_ERR_SHAPE, "%s: cols=%lld is not a multiple of %lld", fn, (long long)cols, (long long)col_mult);
   if (rows == 0 || cols == 0) return MX_OK;
   if (!x || !q || !s) return fail(MX_ERR_NULL, "%s: null pointer (x=%p q=%p s=%p)", fn, x, q, s);
   if (!aligned(x, 16) || !aligned(q, 16))
@@ -109,10 +113,8 @@ const char* mx_version(void) { return "mxmoe 0.1.0 (gfx950)"; }
 
 mx_status mx_quantize_rowwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s,
                               void* stream) {
-  mx_status st = check_quant("mx_quantize_rowwise", x, batch, rows, cols, q, s);
+  mx_status st = check_quant("mx_quantize_rowwise", x, batch, rows, cols, q, s, 1, 32);
   if (st != MX_OK) return st;
-  if (cols % 32 != 0) return fail(MX_ERR_SHAPE, "mx_quantize_rowwise: cols=%lld is not a multiple of 32",
-                                  (long long)cols);
   if (rows == 0 || cols == 0) return MX_OK;
   return hip_status(mxk::launch_quant_rowwise(x, batch * rows, cols, q, s, (hipStream_t)stream),
                     "mx_quantize_rowwise launch");
@@ -120,12 +122,8 @@ mx_status mx_quantize_rowwise(const uint16_t* x, int64_t batch, int64_t rows, in
 
 mx_status mx_quantize_colwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q_t,
                               uint8_t* s_t, void* stream) {
-  mx_status st = check_quant("mx_quantize_colwise", x, batch, rows, cols, q_t, s_t);
+  mx_status st = check_quant("mx_quantize_colwise", x, batch, rows, cols, q_t, s_t, 32, 8);
   if (st != MX_OK) return st;
-  if (rows % 32 != 0) return fail(MX_ERR_SHAPE, "mx_quantize_colwise: rows=%lld is not a multiple of 32",
-                                  (long long)rows);
-  if (cols % 8 != 0) return fail(MX_ERR_SHAPE, "mx_quantize_colwise: cols=%lld is not a multiple of 8",
-                                 (long long)cols);
   if (rows == 0 || cols == 0) return MX_OK;
   if ((rows + 127) / 128 > 65535 || batch > 65535)
     return fail(MX_ERR_SHAPE, "mx_quantize_colwise: rows or batch too large for one launch");
@@ -136,21 +134,21 @@ mx_status mx_quantize_colwise(const uint16_t* x, int64_t batch, int64_t rows, in
 
 mx_status mx_quantize_32x32(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q, uint8_t* s,
                             void* stream) {
-  mx_status st = check_quant("mx_quantize_32x32", x, batch, rows, cols, q, s);
+  mx_status st = check_quant("mx_quantize_32x32", x, batch, rows, cols, q, s, 32, 32);
   if (st != MX_OK) return st;
-  if (rows % 32 != 0 || cols % 32 != 0)
-    return fail(MX_ERR_SHAPE, "mx_quantize_32x32: rows=%lld and cols=%lld must be multiples of 32",
-                (long long)rows, (long long)cols);
   if (rows == 0 || cols == 0) return MX_OK;
   if (batch * rows / 32 > 65535) return fail(MX_ERR_SHAPE, "mx_quantize_32x32: too many row blocks for one launch");
   return hip_status(mxk::launch_quant_32x32(x, batch * rows, cols, q, s, (hipStream_t)stream),
                     "mx_quantize_32x32 launch");
 }
 
-mx_status mx_grouped_gemm_mx(const uint8_t* X, const uint8_t* sX, const uint8_t* Y, const uint8_t* sY,
-                             const int32_t* offs, int mode, int64_t I, int64_t J, int64_t Kc, int64_t E, uint16_t* C,
-                             void* stream) {
-  const char* fn = "mx_grouped_gemm_mx";
+}  // extern "C"
+
+namespace {
+
+mx_status grouped_gemm_impl(const char* fn, const uint8_t* X, const uint8_t* sX, const uint8_t* Y,
+                            const uint8_t* sY, const int32_t* offs, int mode, int64_t I, int64_t J, int64_t Kc,
+                            int64_t E, void* C, int out_f32, void* stream) {
   if (mode != 0 && mode != 1) return fail(MX_ERR_SHAPE, "%s: mode must be 0 or 1 (got %d)", fn, mode);
   if (I < 0 || J < 0 || Kc < 0) return fail(MX_ERR_SHAPE, "%s: negative size", fn);
   if (E < 1 || E > mxk::kMaxExperts)
@@ -171,6 +169,7 @@ mx_status mx_grouped_gemm_mx(const uint8_t* X, const uint8_t* sX, const uint8_t*
   a.sY = sY;
   a.offs = offs;
   a.C = C;
+  a.out_f32 = out_f32;
   a.I = I;
   a.J = J;
   a.Kc = Kc;
@@ -186,7 +185,23 @@ mx_status mx_grouped_gemm_mx(const uint8_t* X, const uint8_t* sX, const uint8_t*
   a.sy_total_per_e = J * (Kc / 32);
   a.ldc = J;
   a.c_estride = I * J;
-  return hip_status(mxk::launch_grouped_gemm(a, (hipStream_t)stream), "mx_grouped_gemm_mx launch");
+  return hip_status(mxk::launch_grouped_gemm(a, (hipStream_t)stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+mx_status mx_grouped_gemm_mx(const uint8_t* X, const uint8_t* sX, const uint8_t* Y, const uint8_t* sY,
+                             const int32_t* offs, int mode, int64_t I, int64_t J, int64_t Kc, int64_t E, uint16_t* C,
+                             void* stream) {
+  return grouped_gemm_impl("mx_grouped_gemm_mx", X, sX, Y, sY, offs, mode, I, J, Kc, E, C, 0, stream);
+}
+
+mx_status mx_grouped_gemm_mx_f32(const uint8_t* X, const uint8_t* sX, const uint8_t* Y, const uint8_t* sY,
+                                 const int32_t* offs, int mode, int64_t I, int64_t J, int64_t Kc, int64_t E, float* C,
+                                 void* stream) {
+  return grouped_gemm_impl("mx_grouped_gemm_mx_f32", X, sX, Y, sY, offs, mode, I, J, Kc, E, C, 1, stream);
 }
 
 size_t mx_grouped_mm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int64_t E) {

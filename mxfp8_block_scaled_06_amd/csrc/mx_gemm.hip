@@ -214,7 +214,7 @@ __device__ __forceinline__ void issue_stage(uint8_t* stage, const uint8_t* Xg, c
   }
 }
 
-template <int MODE>
+template <int MODE, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   __shared__ int s_offs[kMaxExpertsLds];
@@ -333,13 +333,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
 
   // epilogue: lane holds output row i = i0 + iw*128 + qx*32 + l32 and, for
   // register group g, columns j0 + jw*128 + qy*32 + 8g + 4*half + 0..3.
-  uint16_t* Cg = a.C + (MODE == 1 ? (int64_t)td.e * a.c_estride : 0);
+  const int64_t c_off = MODE == 1 ? (int64_t)td.e * a.c_estride : 0;
   const int64_t i_lim = MODE == 0 ? td.i_end : a.I;
 #pragma unroll
   for (int qx = 0; qx < 4; ++qx) {
     const int64_t i = td.i0 + iw * 128 + qx * 32 + l32;
     if (i >= i_lim) continue;
-    uint16_t* crow = Cg + i * a.ldc;
 #pragma unroll
     for (int qy = 0; qy < 4; ++qy) {
 #pragma unroll
@@ -347,10 +346,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
         const int64_t j = td.j0 + jw * 128 + qy * 32 + 8 * g + 4 * half;
         if (j < a.J) {
           const v16f& v = acc[qy][qx];
-          v2i w;
-          w[0] = (int)pack_bf16x2(v[4 * g + 0], v[4 * g + 1]);
-          w[1] = (int)pack_bf16x2(v[4 * g + 2], v[4 * g + 3]);
-          *(v2i*)(crow + j) = w;
+          if (OUT_F32) {
+            float* crow = (float*)a.C + c_off + i * a.ldc;
+            *(float4*)(crow + j) = make_float4(v[4 * g + 0], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+          } else {
+            uint16_t* crow = (uint16_t*)a.C + c_off + i * a.ldc;
+            v2i w;
+            w[0] = (int)pack_bf16x2(v[4 * g + 0], v[4 * g + 1]);
+            w[1] = (int)pack_bf16x2(v[4 * g + 2], v[4 * g + 3]);
+            *(v2i*)(crow + j) = w;
+          }
         }
       }
     }
@@ -370,13 +375,21 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t st) {
   const int64_t grid = (tiles + 7) / 8 * 8;
   if (tiles == 0) return hipSuccess;
   const size_t lds = gemm_lds_bytes();
-  const void* fn = a.mode == 0 ? (const void*)grouped_gemm_kernel<0> : (const void*)grouped_gemm_kernel<1>;
+  const void* fn;
+  if (a.out_f32) {
+    fn = a.mode == 0 ? (const void*)grouped_gemm_kernel<0, true> : (const void*)grouped_gemm_kernel<1, true>;
+  } else {
+    fn = a.mode == 0 ? (const void*)grouped_gemm_kernel<0, false> : (const void*)grouped_gemm_kernel<1, false>;
+  }
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
+  const dim3 g3((unsigned)grid), b3(kThreads);
   if (a.mode == 0) {
-    hipLaunchKernelGGL(grouped_gemm_kernel<0>, dim3((unsigned)grid), dim3(kThreads), lds, st, a);
+    if (a.out_f32) hipLaunchKernelGGL((grouped_gemm_kernel<0, true>), g3, b3, lds, st, a);
+    else hipLaunchKernelGGL((grouped_gemm_kernel<0, false>), g3, b3, lds, st, a);
   } else {
-    hipLaunchKernelGGL(grouped_gemm_kernel<1>, dim3((unsigned)grid), dim3(kThreads), lds, st, a);
+    if (a.out_f32) hipLaunchKernelGGL((grouped_gemm_kernel<1, true>), g3, b3, lds, st, a);
+    else hipLaunchKernelGGL((grouped_gemm_kernel<1, false>), g3, b3, lds, st, a);
   }
   return hipGetLastError();
 }

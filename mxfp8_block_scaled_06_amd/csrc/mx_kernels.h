@@ -14,7 +14,8 @@ struct GemmArgs {
   const uint8_t* Y;
   const uint8_t* sY;
   const int32_t* offs;
-  uint16_t* C;
+  void* C;                    // bf16 (uint16_t) or fp32 output
+  int out_f32;                // 1: fp32 output, 0: bf16 (RNE)
   int64_t I, J, Kc;
   int E;
   int mode;

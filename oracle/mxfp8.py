@@ -229,24 +229,26 @@ def group_bounds(offs: np.ndarray, M: int):
     return [(int(a), int(b)) for a, b in zip(starts, offs)]
 
 
-def grouped_gemm_mx(X, sX, Y, sY, offs, mode: int) -> np.ndarray:
+def grouped_gemm_mx(X, sX, Y, sY, offs, mode: int, absolute: bool = False) -> np.ndarray:
     """The GEMM on prequantized operands, in fp64.
 
     C[i, j] = sum_k deq(X)[i, k] * deq(Y)[j, k], blocks of 32 along k.
     mode 0: groups over the rows i of X; Y is [E, J, Kc]; C is [I, J].
     mode 1: groups over the contraction k; X is [I, Kc], Y is [J, Kc]; C is [E, I, J].
+    absolute=True sums |deq(X)| |deq(Y)| instead (the error-bound companion).
     """
-    dX = dequant_rowwise(X, sX)
+    f = np.abs if absolute else (lambda v: v)
+    dX = f(dequant_rowwise(X, sX))
     if mode == 0:
         I = dX.shape[0]
         J = Y.shape[1]
         C = np.zeros((I, J), dtype=np.float64)
         for e, (a, b) in enumerate(group_bounds(offs, I)):
             if b > a:
-                C[a:b] = dX[a:b] @ dequant_rowwise(Y[e], sY[e]).T
+                C[a:b] = dX[a:b] @ f(dequant_rowwise(Y[e], sY[e])).T
         return C
     if mode == 1:
-        dY = dequant_rowwise(Y, sY)
+        dY = f(dequant_rowwise(Y, sY))
         E = len(offs)
         C = np.zeros((E, dX.shape[0], dY.shape[0]), dtype=np.float64)
         for e, (a, b) in enumerate(group_bounds(offs, dX.shape[1])):
@@ -256,42 +258,46 @@ def grouped_gemm_mx(X, sX, Y, sY, offs, mode: int) -> np.ndarray:
     raise ValueError(mode)
 
 
-def grouped_mm_fwd(A_bits, W_bits, offs) -> np.ndarray:
-    """out[g_e] = MX(A)[g_e] @ MX(W[e])^T; A rowwise along K, W rowwise along K."""
+def grouped_mm_fwd(A_bits, W_bits, offs, absolute: bool = False) -> np.ndarray:
+    """out[g_e] = MX(A)[g_e] @ MX(W[e])^T; A rowwise along K, W rowwise along K.
+    absolute=True gives sum_k |a_k w_k| instead (error-bound companion)."""
+    f = np.abs if absolute else (lambda v: v)
     qA, sA = quantize_rowwise(A_bits)
     M = qA.shape[0]
     N = W_bits.shape[1]
     out = np.zeros((M, N), dtype=np.float64)
-    dA = dequant_rowwise(qA, sA)
+    dA = f(dequant_rowwise(qA, sA))
     for e, (a, b) in enumerate(group_bounds(offs, M)):
         if b > a:
             qW, sW = quantize_rowwise(W_bits[e])
-            out[a:b] = dA[a:b] @ dequant_rowwise(qW, sW).T
+            out[a:b] = dA[a:b] @ f(dequant_rowwise(qW, sW)).T
     return out
 
 
-def grouped_mm_dgrad(dOut_bits, W_bits, offs) -> np.ndarray:
+def grouped_mm_dgrad(dOut_bits, W_bits, offs, absolute: bool = False) -> np.ndarray:
     """dA[g_e] = MX(dOut)[g_e] @ MX_t(W[e]); dOut rowwise along N, W blocked
     along N (stored [K, N]), contraction over N."""
+    f = np.abs if absolute else (lambda v: v)
     qG, sG = quantize_rowwise(dOut_bits)
     M = qG.shape[0]
     K = W_bits.shape[2]
-    dG = dequant_rowwise(qG, sG)
+    dG = f(dequant_rowwise(qG, sG))
     out = np.zeros((M, K), dtype=np.float64)
     for e, (a, b) in enumerate(group_bounds(offs, M)):
         if b > a:
             qWt, sWt = quantize_colwise(W_bits[e])              # [K, N], [K, N/32]
-            out[a:b] = dG[a:b] @ dequant_rowwise(qWt, sWt).T
+            out[a:b] = dG[a:b] @ f(dequant_rowwise(qWt, sWt)).T
     return out
 
 
-def grouped_mm_wgrad(dOut_bits, A_bits, offs) -> np.ndarray:
+def grouped_mm_wgrad(dOut_bits, A_bits, offs, absolute: bool = False) -> np.ndarray:
     """dW[e] = MX_t(dOut)[:, g_e] @ MX_t(A)[:, g_e]^T with both operands blocked
     along tokens; an expert with no tokens gets zeros (reading R-empty)."""
+    f = np.abs if absolute else (lambda v: v)
     qGt, sGt = quantize_colwise(dOut_bits)                      # [N, M]
     qAt, sAt = quantize_colwise(A_bits)                         # [K, M]
-    dGt = dequant_rowwise(qGt, sGt)
-    dAt = dequant_rowwise(qAt, sAt)
+    dGt = f(dequant_rowwise(qGt, sGt))
+    dAt = f(dequant_rowwise(qAt, sAt))
     E = len(offs)
     out = np.zeros((E, dGt.shape[0], dAt.shape[0]), dtype=np.float64)
     for e, (a, b) in enumerate(group_bounds(offs, dGt.shape[1])):

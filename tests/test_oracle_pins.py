@@ -326,3 +326,18 @@ def test_r1_accepts_rounded_oracle_and_rejects_one_bad_block():
     bad = r.copy()
     bad[3, 32:64] *= 2.0                # one block's scale off by one binade
     assert not oracle.r1_check(inp.f32_to_bf16_bits(bad.astype(np.float32)), r)["ok"]
+
+
+def test_absolute_companion_bounds_the_sum():
+    """sum_k |x_k y_k| (the error-bound companion) equals the plain sum when
+    every operand is non-negative, and bounds |sum| otherwise."""
+    counts = [32, 0, 64]
+    offs = inp.offsets_from_counts(counts)
+    A = inp.random_bf16((96, 128), seed=61, outliers=True)
+    W = inp.random_bf16((3, 64, 128), seed=62, std=0.02)
+    G = inp.random_bf16((96, 64), seed=63, std=1e-3)
+    for fn, a, b in ((oracle.grouped_mm_fwd, A, W), (oracle.grouped_mm_dgrad, G, W), (oracle.grouped_mm_wgrad, G, A)):
+        plain, absd = fn(a, b, offs), fn(a, b, offs, absolute=True)
+        assert (absd >= np.abs(plain) - 1e-12 * absd).all()
+        pos = (a & 0x7FFF, b & 0x7FFF)                          # clear sign bits
+        np.testing.assert_allclose(fn(*pos, offs, absolute=True), fn(*pos, offs), rtol=1e-12)
