@@ -189,10 +189,12 @@ def main():
     log(f"step {ms_per_step:.3f} ms ({prim_ms}); wall {wall:.2f}s for {args.steps} steps")
 
     # ---------------- GEMM only, prequantized operands ----------------
+    g = mx.mx_scales_to_gemm_layout
     qA, sA = mx.mx_quantize_rowwise(A)
     qW, sW = mx.mx_quantize_rowwise(W)
     qG, sG = mx.mx_quantize_rowwise(G)
     qWt, sWt = mx.mx_quantize_colwise(W)
+    sA, sW, sG, sWt = g(sA), g(sW), g(sG), g(sWt)
     # wgrad operands: the token axis is the contraction axis, padded to a
     # multiple of 128 with zero rows (the layout the bf16 entry point uses)
     Mp = (M + 127) // 128 * 128
@@ -202,6 +204,7 @@ def main():
     Ap[:M] = A
     qGt, sGt = mx.mx_quantize_colwise(Gp)
     qAt, sAt = mx.mx_quantize_colwise(Ap)
+    sGt, sAt = g(sGt), g(sAt)
     del Gp, Ap
     c_fwd = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     c_dg = torch.empty((M, K), dtype=torch.bfloat16, device=dev)

@@ -105,6 +105,18 @@ mx_status mx_quantize_32x32(const uint16_t* x, int64_t batch, int64_t rows, int6
                             uint8_t* q, uint8_t* s, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Scale layout conversion for the GEMM.  The quantizers above write scales
+ * row-major, [batch, rows, kblocks].  The GEMM reads them in its blocked
+ * layout [batch, kblocks/4, rows, 4]: element (b, r, kb) moves to
+ * ((b * kblocks/4 + kb/4) * rows + r) * 4 + kb%4, so the four scale blocks of
+ * one 128-element contraction step of consecutive rows are contiguous (the
+ * role of the per-group blocked scale conversion in the pytorch/ao PR
+ * timeline).  Requires kblocks % 4 == 0; s_gemm 4-byte aligned.
+ * ------------------------------------------------------------------------ */
+mx_status mx_scales_to_gemm_layout(const uint8_t* s, int64_t batch, int64_t rows, int64_t kblocks,
+                                   uint8_t* s_gemm, void* stream);
+
+/* ------------------------------------------------------------------------
  * The block-scaled grouped GEMM on prequantized operands.
  *
  *   C[i, j] = sum_k X[i, k] * Y[j, k] * 2^(sX[i, k/32] + sY[j, k/32] - 254)
@@ -117,6 +129,9 @@ mx_status mx_quantize_32x32(const uint16_t* x, int64_t batch, int64_t rows, int6
  *           X [I, Kc], Y [J, Kc] (token axis contiguous), C [E, I, J];
  *           expert e sums k in [offs[e-1], offs[e]); an empty group gives
  *           C[e] = 0.  Group starts must be multiples of 32.
+ * Scale tensors are passed in the GEMM layout of mx_scales_to_gemm_layout
+ * (sX with batch 1 and rows I; sY with batch E and rows J in mode 0, batch 1
+ * and rows J in mode 1).
  * offs: int32 [E] cumulative END offsets on the device (offs[-1] = 0),
  * over rows of X (mode 0) or over k (mode 1).
  * Requires Kc % 128 == 0, J % 8 == 0, E >= 1.

@@ -17,7 +17,7 @@ from typing import Optional, Tuple
 __all__ = [
     "MXError", "library_path", "load_library", "version",
     "mx_quantize_rowwise", "mx_quantize_colwise", "mx_quantize_32x32",
-    "mx_grouped_gemm_mx", "mx_grouped_gemm_mx_f32", "mx_grouped_mm_workspace_bytes",
+    "mx_grouped_gemm_mx", "mx_grouped_gemm_mx_f32", "mx_grouped_mm_workspace_bytes", "mx_scales_to_gemm_layout",
     "mx_grouped_mm_fwd", "mx_grouped_mm_dgrad", "mx_grouped_mm_wgrad",
     "OP_FWD", "OP_DGRAD", "OP_WGRAD",
 ]
@@ -62,6 +62,8 @@ def load_library():
         f = getattr(lib, name)
         f.restype = c_int
         f.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp]
+    lib.mx_scales_to_gemm_layout.restype = c_int
+    lib.mx_scales_to_gemm_layout.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]
     lib.mx_grouped_mm_workspace_bytes.restype = c_sz
     lib.mx_grouped_mm_workspace_bytes.argtypes = [c_int, c_i64, c_i64, c_i64, c_i64]
     for name in ("mx_grouped_mm_fwd", "mx_grouped_mm_dgrad", "mx_grouped_mm_wgrad"):
@@ -160,13 +162,27 @@ def mx_quantize_32x32(x, q=None, s=None):
     return q, s
 
 
+def mx_scales_to_gemm_layout(s, out=None):
+    """Row-major scales [B?, R, KB] -> the GEMM's blocked layout [B?, KB/4, R, 4]."""
+    import torch
+    lib = load_library()
+    _require(s, torch.uint8, "s")
+    B, R, KB = _as3d(s)
+    if out is None:
+        out = torch.empty((*s.shape[:-2], KB // 4, R, 4), dtype=torch.uint8, device=s.device)
+    _check("mx_scales_to_gemm_layout",
+           lib.mx_scales_to_gemm_layout(_ptr(s), B, R, KB, _ptr(out), _stream(s.device)))
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Grouped GEMM on prequantized operands
 # ---------------------------------------------------------------------------
 def mx_grouped_gemm_mx(X, sX, Y, sY, offs, mode: int, out=None, out_dtype=None):
     """C[i,j] = sum_k X[i,k] Y[j,k] 2^(sX+sY-254).  mode 0: Y [E,J,Kc], C [I,J];
-    mode 1 (groups over k): Y [J,Kc], C [E,I,J].  Returns C (bf16, or fp32
-    with out_dtype=torch.float32)."""
+    mode 1 (groups over k): Y [J,Kc], C [E,I,J].  Scales sX, sY are in the
+    GEMM layout (mx_scales_to_gemm_layout).  Returns C (bf16, or fp32 with
+    out_dtype=torch.float32)."""
     import torch
     lib = load_library()
     if out_dtype is None:

@@ -116,7 +116,7 @@ mx_status mx_quantize_rowwise(const uint16_t* x, int64_t batch, int64_t rows, in
   mx_status st = check_quant("mx_quantize_rowwise", x, batch, rows, cols, q, s, 1, 32);
   if (st != MX_OK) return st;
   if (rows == 0 || cols == 0) return MX_OK;
-  return hip_status(mxk::launch_quant_rowwise(x, batch * rows, cols, q, s, (hipStream_t)stream),
+  return hip_status(mxk::launch_quant_rowwise(x, batch * rows, cols, q, s, 0, (hipStream_t)stream),
                     "mx_quantize_rowwise launch");
 }
 
@@ -128,7 +128,7 @@ mx_status mx_quantize_colwise(const uint16_t* x, int64_t batch, int64_t rows, in
   if ((rows + 127) / 128 > 65535 || batch > 65535)
     return fail(MX_ERR_SHAPE, "mx_quantize_colwise: rows or batch too large for one launch");
   return hip_status(
-      mxk::launch_quant_colwise(x, batch, rows, cols, q_t, rows, s_t, rows / 32, (hipStream_t)stream),
+      mxk::launch_quant_colwise(x, batch, rows, cols, q_t, rows, s_t, rows / 32, 0, (hipStream_t)stream),
       "mx_quantize_colwise launch");
 }
 
@@ -176,13 +176,8 @@ mx_status grouped_gemm_impl(const char* fn, const uint8_t* X, const uint8_t* sX,
   a.E = (int)E;
   a.mode = mode;
   a.ldx = Kc;
-  a.ldsx = Kc / 32;
-  a.ldy = Kc;
-  a.ldsy = Kc / 32;
   a.y_estride = J * Kc;
   a.sy_estride = J * (Kc / 32);
-  a.sx_total = I * (Kc / 32);
-  a.sy_total_per_e = J * (Kc / 32);
   a.ldc = J;
   a.c_estride = I * J;
   return hip_status(mxk::launch_grouped_gemm(a, (hipStream_t)stream), fn);
@@ -204,6 +199,19 @@ mx_status mx_grouped_gemm_mx_f32(const uint8_t* X, const uint8_t* sX, const uint
   return grouped_gemm_impl("mx_grouped_gemm_mx_f32", X, sX, Y, sY, offs, mode, I, J, Kc, E, C, 1, stream);
 }
 
+mx_status mx_scales_to_gemm_layout(const uint8_t* s, int64_t batch, int64_t rows, int64_t kblocks, uint8_t* s_gemm,
+                                   void* stream) {
+  const char* fn = "mx_scales_to_gemm_layout";
+  if (batch < 1 || rows < 0 || kblocks < 0)
+    return fail(MX_ERR_SHAPE, "%s: batch=%lld rows=%lld kblocks=%lld", fn, (long long)batch, (long long)rows,
+                (long long)kblocks);
+  if (kblocks % 4 != 0) return fail(MX_ERR_SHAPE, "%s: kblocks=%lld is not a multiple of 4", fn, (long long)kblocks);
+  if (rows == 0 || kblocks == 0) return MX_OK;
+  if (!s || !s_gemm) return fail(MX_ERR_NULL, "%s: null pointer", fn);
+  if (!aligned(s_gemm, 4)) return fail(MX_ERR_ALIGN, "%s: s_gemm must be 4-byte aligned", fn);
+  return hip_status(mxk::launch_scales_to_gemm(s, batch, rows, kblocks, s_gemm, (hipStream_t)stream), fn);
+}
+
 size_t mx_grouped_mm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int64_t E) {
   if (op < MX_OP_FWD || op > MX_OP_WGRAD || M < 0 || N < 0 || K < 0 || E < 1) return 0;
   return ws_layout(op, M, N, K, E).total;
@@ -221,11 +229,12 @@ mx_status mx_grouped_mm_fwd(const uint16_t* A, const uint16_t* W, const int32_t*
     return fail(MX_ERR_WORKSPACE, "%s: workspace of %zu bytes at %p, need %zu", fn, ws_bytes, ws, L.total);
   if (!aligned(ws, 256)) return fail(MX_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
   if (M == 0 || N == 0) return MX_OK;
+  if ((E * N + M) * (K / 32) >= ((int64_t)1 << 31)) return fail(MX_ERR_SHAPE, "%s: tensors too large", fn);
   uint8_t* w8 = (uint8_t*)ws;
   hipStream_t s = (hipStream_t)stream;
   uint8_t *qA = w8 + L.off[0], *sA = w8 + L.off[1], *qW = w8 + L.off[2], *sW = w8 + L.off[3];
-  if ((st = hip_status(mxk::launch_quant_rowwise(A, M, K, qA, sA, s), "fwd quantize A")) != MX_OK) return st;
-  if ((st = hip_status(mxk::launch_quant_rowwise(W, E * N, K, qW, sW, s), "fwd quantize W")) != MX_OK) return st;
+  if ((st = hip_status(mxk::launch_quant_rowwise(A, M, K, qA, sA, M, s), "fwd quantize A")) != MX_OK) return st;
+  if ((st = hip_status(mxk::launch_quant_rowwise(W, E * N, K, qW, sW, N, s), "fwd quantize W")) != MX_OK) return st;
   return mx_grouped_gemm_mx(qA, sA, qW, sW, offs, 0, M, N, K, E, out, stream);
 }
 
@@ -245,9 +254,10 @@ mx_status mx_grouped_mm_dgrad(const uint16_t* dOut, const uint16_t* W, const int
   uint8_t* w8 = (uint8_t*)ws;
   hipStream_t s = (hipStream_t)stream;
   uint8_t *qG = w8 + L.off[0], *sG = w8 + L.off[1], *qWt = w8 + L.off[2], *sWt = w8 + L.off[3];
-  if ((st = hip_status(mxk::launch_quant_rowwise(dOut, M, N, qG, sG, s), "dgrad quantize dOut")) != MX_OK) return st;
+  if ((st = hip_status(mxk::launch_quant_rowwise(dOut, M, N, qG, sG, M, s), "dgrad quantize dOut")) != MX_OK)
+    return st;
   // W [E, N, K] quantized in 32-blocks along N, stored transposed [E, K, N]
-  if ((st = hip_status(mxk::launch_quant_colwise(W, E, N, K, qWt, N, sWt, N / 32, s), "dgrad quantize W")) != MX_OK)
+  if ((st = hip_status(mxk::launch_quant_colwise(W, E, N, K, qWt, N, sWt, N / 32, 1, s), "dgrad quantize W")) != MX_OK)
     return st;
   return mx_grouped_gemm_mx(qG, sG, qWt, sWt, offs, 0, M, K, N, E, dA, stream);
 }
@@ -271,10 +281,11 @@ mx_status mx_grouped_mm_wgrad(const uint16_t* dOut, const uint16_t* A, const int
   hipStream_t s = (hipStream_t)stream;
   uint8_t *qGt = w8 + L.off[0], *sGt = w8 + L.off[1], *qAt = w8 + L.off[2], *sAt = w8 + L.off[3];
   // dOut [M, N] and A [M, K] in 32-blocks along tokens, stored [N, Mp] and [K, Mp]
-  if ((st = hip_status(mxk::launch_quant_colwise(dOut, 1, M, N, qGt, Mp, sGt, Mp / 32, s), "wgrad quantize dOut")) !=
+  if ((st = hip_status(mxk::launch_quant_colwise(dOut, 1, M, N, qGt, Mp, sGt, Mp / 32, 1, s), "wgrad quantize dOut")) !=
       MX_OK)
     return st;
-  if ((st = hip_status(mxk::launch_quant_colwise(A, 1, M, K, qAt, Mp, sAt, Mp / 32, s), "wgrad quantize A")) != MX_OK)
+  if ((st = hip_status(mxk::launch_quant_colwise(A, 1, M, K, qAt, Mp, sAt, Mp / 32, 1, s), "wgrad quantize A")) !=
+      MX_OK)
     return st;
   return mx_grouped_gemm_mx(qGt, sGt, qAt, sAt, offs, 1, N, K, Mp, E, dW, stream);
 }

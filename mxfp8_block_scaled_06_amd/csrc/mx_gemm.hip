@@ -20,21 +20,28 @@
 //  * The A operand of the MFMA is Y and the B operand is X, so each lane's
 //    accumulators hold four consecutive output columns of one output row:
 //    the bf16 epilogue writes 8-byte runs without an LDS round trip.
-//  * Workgroup tile 256 x 256 x 128 bytes, 4 waves of 128 x 128 (4x4 MFMA
-//    tiles each, 256 fp32 accumulators per lane).  Operand tiles move
-//    HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging), double
-//    buffered (2 x 68 KiB of the 160 KiB LDS), 16-byte pieces XOR-swizzled
-//    by row to spread LDS banks.
+//  * Workgroup tile 256 x 256, 4 waves of 128 x 128 (4x4 MFMA tiles each,
+//    256 fp32 accumulators per lane in AGPRs).  Stages of 128 contraction
+//    bytes: every row moves as one full 128-byte line, HBM/L2 -> LDS by
+//    buffer_load ... lds (no VGPR staging), two stages of 68 KiB in LDS.
+//    Buffer descriptors end at the last valid row, so rows past a group end
+//    read as zeros without clamping code.  Scales use the GEMM layout
+//    [K/128][rows][4] so one stage's scales for 256 rows are one 1 KiB line
+//    run per operand.
+//  * Operand fragments roll through registers: each 32-row fragment is
+//    refilled from LDS as soon as its last MFMA has issued, so LDS latency
+//    hides behind the remaining MFMAs.  One barrier per stage, placed after
+//    the first MFMAs of the stage's second half: past it, every wave has
+//    finished reading the other LDS buffer, which then receives the loads of
+//    the stage after next (a full stage of latency budget).
 //  * Tile scheduler on the device: the group offsets never cross to the host.
 //    Mode 0 enumerates (expert, M-tile) pairs from the offsets; tiles are
 //    ordered in bands of 8 N-tiles so concurrently running workgroups share
 //    operand rows, and the workgroup id is remapped so each XCD (workgroups
 //    are dealt round-robin over the 8 XCDs) receives a contiguous slice of the
 //    tile order, keeping the shared rows in that XCD's L2.
-//  * Ragged groups: rows past a group end are clamped to the last valid row
-//    on load and masked on store; K blocks past the end of the range (mode 1
-//    group ends, or Kc not a multiple of 128) are zeroed in registers with
-//    their scale forced to 1.  Empty wgrad groups store zeros.
+//  * K blocks past the end of a wgrad group are zeroed in registers with a
+//    neutral scale; empty wgrad groups store zeros.
 #include "mx_device.h"
 #include "mx_kernels.h"
 
@@ -42,17 +49,34 @@ namespace mxk {
 
 constexpr int kBM = 256;        // output rows per tile (rows of X)
 constexpr int kBN = 256;        // output cols per tile (rows of Y)
-constexpr int kBK = 128;        // contraction bytes per stage (4 scale blocks)
+constexpr int kBK = 128;        // contraction bytes per stage (4 scale blocks, 2 MFMA windows)
 constexpr int kThreads = 256;   // 4 waves, 2 x 2 arrangement of 128 x 128
 constexpr int kBand = 8;        // N-tiles per band in the tile order
 constexpr int kTileBytes = kBM * kBK;             // 32 KiB per operand tile
-constexpr int kScaleBytes = kBM * 8;              // 8 scale bytes per row staged
-constexpr int kStageBytes = 2 * kTileBytes + 2 * kScaleBytes;
+constexpr int kScaleChunk = kBM * 4;              // one [rows][4] scale chunk: 1 KiB
+constexpr int kStageBytes = 2 * kTileBytes + 4 * kScaleChunk;
+constexpr int kDmaPerStage = 8 + 8 + 1;           // per wave: X data, Y data, one scale chunk
 constexpr int kMaxExpertsLds = 1024;
+constexpr int kRsrcWord3 = 0x00020000;            // raw buffer, 32-bit elements (gfx9 family)
 
 static_assert(kBM == kBN, "operand tiles share the load code");
 
+// 16-byte piece swizzle of a 128-byte LDS row: the 32 lanes that read one
+// logical piece of 32 consecutive rows spread over all bank groups.
 __device__ __forceinline__ int piece_swz(int row) { return (row >> 1) & 7; }
+
+__device__ __forceinline__ int64_t uni64(int64_t v) {
+  const uint64_t u = (uint64_t)v;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ int uni32(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (bytes < 0 ? 0 : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcWord3);
+}
 
 struct TileDesc {
   int valid;
@@ -116,14 +140,13 @@ __device__ __forceinline__ TileDesc decode_tile(const GemmArgs& a, int* s_offs, 
     const int64_t width = min((int64_t)kBand, ntj - band * kBand);
     const int64_t mt = within / width;
     const int64_t nt = band * kBand + within % width;
-    // expert of M-tile mt: last e with pref[e] <= mt (binary search)
+    // expert owning M-tile mt: the last e with pref[e] <= mt (experts without
+    // tiles share their successor's prefix and are skipped by this rule)
     int lo = 0, hi = a.E - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (s_pref[mid] <= mt) lo = mid; else hi = mid - 1;
     }
-    // experts without tiles share their successor's prefix; the search picks
-    // the last expert whose prefix is <= mt, which owns tile mt
     const int e = lo;
     int64_t st = e == 0 ? 0 : s_offs[e - 1];
     int64_t en = s_offs[e];
@@ -167,79 +190,165 @@ __device__ __forceinline__ TileDesc decode_tile(const GemmArgs& a, int* s_offs, 
   return d;
 }
 
-// Issue the DMA loads of one stage: operand data (8 x 1 KiB per wave per
-// operand) and the 8 scale bytes per row that cover the stage's 4 blocks.
-__device__ __forceinline__ void issue_stage(uint8_t* stage, const uint8_t* Xg, const uint8_t* sXg,
-                                            const uint8_t* Yg, const uint8_t* sYg, int64_t x_rows_lo,
-                                            int64_t x_rows_hi, int64_t y_rows_hi, int64_t ldx, int64_t ldsx,
-                                            int64_t ldy, int64_t ldsy, int64_t sx_total, int64_t sy_total,
-                                            int64_t kk, int64_t k0, int64_t k1) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // LDS DMA bases must be wave-uniform
-  uint8_t* xs = stage;
-  uint8_t* ys = stage + kTileBytes;
-  uint8_t* sxs = stage + 2 * kTileBytes;
-  uint8_t* sys = sxs + kScaleBytes;
-  // data: 32 chunks of 1 KiB (8 rows x 128 B) per operand, 8 per wave
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int c = wv * 8 + u;
-    const int row = c * 8 + (lane >> 3);
-    const int logical = (lane & 7) ^ piece_swz(row);
-    int64_t k = kk + logical * 16;
-    if (k >= k1) k = k0;
-    int64_t xr = x_rows_lo + row;
-    if (xr > x_rows_hi) xr = x_rows_hi;
-    int64_t yr = row;  // relative to Yg which already points at row j0
-    if (yr > y_rows_hi) yr = y_rows_hi;
-    __builtin_amdgcn_global_load_lds((const void*)(Xg + xr * ldx + k), (lds_void*)(xs + c * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(Yg + yr * ldy + k), (lds_void*)(ys + c * 1024), 16, 0, 0);
-  }
-  // scales: per row the aligned dword pair covering blocks kk/32 .. kk/32+3
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int pos = wv * 128 + u * 64 + lane;   // 0..511: row = pos/2, dword = pos%2
-    const int row = pos >> 1, dw = pos & 1;
-    int64_t xr = x_rows_lo + row;
-    if (xr > x_rows_hi) xr = x_rows_hi;
-    int64_t yr = row;
-    if (yr > y_rows_hi) yr = y_rows_hi;
-    const int64_t kb = kk >> 5;
-    int64_t px = ((xr * ldsx + kb) & ~(int64_t)3) + 4 * dw;
-    if (px + 4 > sx_total) px -= 4;
-    int64_t py = ((yr * ldsy + kb) & ~(int64_t)3) + 4 * dw;
-    if (py + 4 > sy_total) py -= 4;
-    __builtin_amdgcn_global_load_lds((const void*)(sXg + px), (lds_void*)(sxs + (wv * 2 + u) * 256), 4, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(sYg + py), (lds_void*)(sys + (wv * 2 + u) * 256), 4, 0, 0);
+// Per-tile load state.  Descriptor bases/extents are wave-uniform (SGPRs);
+// the per-lane byte offsets of this lane's 16-byte pieces are fixed for the
+// whole tile, so a stage's loads cost no vector ALU work.
+struct LoadState {
+  const uint8_t* xb;      // X row i0
+  const uint8_t* yb;      // Y row j0 (expert e in mode 0)
+  const uint8_t* sxb;     // X scales, chunk 0, row i0
+  const uint8_t* syb;     // Y scales, chunk 0, row j0
+  int64_t x_bytes, y_bytes;         // valid data bytes from xb / yb
+  int64_t sx_chunk, sy_chunk;       // bytes between scale chunks (rows x 4)
+  int64_t sx_rows4, sy_rows4;       // valid scale bytes per chunk from sxb / syb
+  int64_t nchunks;                  // scale chunks per row (Kc / 128)
+  int voff[8];                      // data piece offsets (X and Y share the row stride)
+};
+
+// DMA of one stage (contraction bytes [k0 + 128*stage_no, +128)) into LDS
+// buffer `buf`: per wave 8 + 8 one-KiB data loads (rows 64*wv .. +63 of X and
+// Y) and one 1 KiB scale chunk (wave 0/1: X chunks q, q+1; wave 2/3: Y chunks
+// q, q+1; chunk q+1 only when the stage is not 4-block aligned).  Stages at or
+// past `ns` get empty ranges: no data moves, but every wave still issues its
+// 17 loads so the vmcnt bookkeeping is the same for every stage.
+struct StageDma {
+  __amdgpu_buffer_rsrc_t rx, ry, rs;
+  uint8_t* st;
+};
+
+__device__ __forceinline__ StageDma make_stage_dma(uint8_t* smem, int buf, const LoadState& L, int64_t k0,
+                                                   int stage_no, int ns, int wv) {
+  StageDma d;
+  d.st = smem + buf * kStageBytes;
+  const bool live = stage_no < ns;
+  const int64_t kk = k0 + (int64_t)stage_no * kBK;
+  d.rx = make_rsrc(L.xb + kk, live ? L.x_bytes - kk : 0);
+  d.ry = make_rsrc(L.yb + kk, live ? L.y_bytes - kk : 0);
+  const int64_t kb = kk >> 5;
+  const int64_t q = (kb >> 2) + (wv & 1);
+  const bool need = live && q < L.nchunks && ((wv & 1) == 0 || (kb & 3) != 0);
+  const bool is_x = wv < 2;
+  const uint8_t* sbase = is_x ? L.sxb + q * L.sx_chunk : L.syb + q * L.sy_chunk;
+  d.rs = make_rsrc(sbase, need ? (is_x ? L.sx_rows4 : L.sy_rows4) : 0);
+  return d;
+}
+
+// Load number `n` (0..16) of a stage's DMA for this wave: even n < 16 move X
+// rows, odd n < 16 Y rows, n == 16 the scale chunk.
+template <int n>
+__device__ __forceinline__ void issue_load(const StageDma& d, const LoadState& L, int wv, int lane) {
+  if (n < 16) {
+    const int u = n >> 1;
+    const int c = wv * 8 + u;   // 1 KiB chunk = 8 rows x 128 B
+    if ((n & 1) == 0) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rx, (lds_void*)(d.st + c * 1024), 16, L.voff[u], 0, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ry, (lds_void*)(d.st + kTileBytes + c * 1024), 16, L.voff[u], 0, 0,
+                                               0);
+    }
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rs, (lds_void*)(d.st + 2 * kTileBytes + wv * kScaleChunk), 16,
+                                             lane * 16, 0, 0, 0);
   }
 }
+
+template <int first, int count>
+__device__ __forceinline__ void issue_loads(const StageDma& d, const LoadState& L, int wv, int lane) {
+  if constexpr (count > 0) {
+    issue_load<first>(d, L, wv, lane);
+    issue_loads<first + 1, count - 1>(d, L, wv, lane);
+  }
+}
+
+// One MFMA operand: 32 rows x 64 K of E4M3 (two 16-byte pieces per lane)
+// and the lane's E8M0 scale byte.
+struct Frag {
+  v8i v;
+  int s;
+};
+
+// Read the operand of one 32-row sub-tile (this lane's `row`) for MFMA window
+// `w` (0/1) of a stage: pieces 4w + half and 4w + half + 2 of the row, and
+// the scale byte of block 2w + half.  `soff` = byte offset of the stage's
+// first block inside the staged scale chunks (0..3).  With MASKED, blocks at
+// or past `nvalid` are zeroed and their scale lanes made neutral.
+template <bool MASKED>
+__device__ __forceinline__ void read_frag(const uint8_t* tile, const uint8_t* sc, int row, int pa, int pb,
+                                          int w, int half, int soff, int nvalid, Frag& f) {
+  const v4i a0 = *(const v4i*)(tile + row * kBK + pa);
+  const v4i a1 = *(const v4i*)(tile + row * kBK + pb);
+  const int t = soff + 2 * w + half;
+  int scale = sc[(t >> 2) * kScaleChunk + row * 4 + (t & 3)];
+  v4i b0 = a0, b1 = a1;
+  if (MASKED) {
+    const int keep0 = (2 * w) < nvalid ? -1 : 0;       // chunk 0 of every lane lies in block 2w
+    const int keep1 = (2 * w + 1) < nvalid ? -1 : 0;   // chunk 1 in block 2w + 1
+    b0 &= (v4i){keep0, keep0, keep0, keep0};
+    b1 &= (v4i){keep1, keep1, keep1, keep1};
+    scale = (2 * w + half) < nvalid ? scale : 127;
+  }
+  f.v = (v8i){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+  f.s = scale;
+}
+
+__device__ __forceinline__ v16f mfma(const Frag& y, const Frag& x, v16f c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(y.v, x.v, c, 0, 0, 0, y.s, 0, x.s);
+}
+
+// All of this wave's loads have landed (the next stage), then workgroup
+// barrier.  One asm statement with a memory clobber: no LDS access moves
+// across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// Prologue: stage 0 landed while the first 12 loads of stage 1 may fly.
+__device__ __forceinline__ void first_barrier() {
+  asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+static_assert(kDmaPerStage == 17, "12 loads of a stage issue in one stage, 5 in the next");
+
+#define MX_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 template <int MODE, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-  __shared__ int s_offs[kMaxExpertsLds];
-  __shared__ int s_pref[kMaxExpertsLds];
+  __shared__ int s_offs[MODE == 0 ? kMaxExpertsLds : 1];
+  __shared__ int s_pref[MODE == 0 ? kMaxExpertsLds : 1];
   __shared__ int s_misc[4];
 
-  const TileDesc td = decode_tile<MODE>(a, s_offs, s_pref, s_misc);
-  if (!td.valid) return;
+  const TileDesc td0 = decode_tile<MODE>(a, s_offs, s_pref, s_misc);
+  if (!td0.valid) return;
 
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = uni32(tid >> 6);
   const int iw = wv >> 1, jw = wv & 1;   // wave's 128x128 quadrant: rows iw, cols jw
   const int half = lane >> 5, l32 = lane & 31;
 
-  // operand bases
-  const uint8_t* Xg = a.X;
-  const uint8_t* sXg = a.sX;
-  const uint8_t* Yg = a.Y + (MODE == 0 ? (int64_t)td.e * a.y_estride : 0) + td.j0 * a.ldy;
-  const uint8_t* sYg = a.sY + (MODE == 0 ? (int64_t)td.e * a.sy_estride : 0);
-  const int64_t x_rows_lo = td.i0;
-  const int64_t x_rows_hi = (MODE == 0 ? td.i_end : a.I) - 1;   // clamp target (valid row)
-  const int64_t y_rows_hi = a.J - 1 - td.j0;                     // relative to j0
-  // scale rows are addressed absolutely: shift Y scale rows by j0
-  const int64_t sy_row0 = td.j0;
-  const int64_t sx_total = a.sx_total;
-  const int64_t sy_total = a.sy_total_per_e;
+  // tile description, made wave-uniform (it is identical for every thread)
+  const int e = uni32(td0.e);
+  const int64_t i0 = uni64(td0.i0), i_end = uni64(td0.i_end), j0 = uni64(td0.j0);
+  const int64_t k0 = uni64(td0.k0), k1 = uni64(td0.k1);
+  const int64_t x_end = MODE == 0 ? i_end : a.I;
+  const int64_t rows_x = min((int64_t)kBM, x_end - i0);
+  const int64_t rows_y = min((int64_t)kBN, a.J - j0);
+
+  LoadState L;
+  L.xb = a.X + i0 * a.ldx;
+  L.yb = a.Y + (MODE == 0 ? (int64_t)e * a.y_estride : 0) + j0 * a.ldx;
+  L.sx_chunk = a.I * 4;
+  L.sy_chunk = a.J * 4;
+  L.sxb = a.sX + i0 * 4;
+  L.syb = a.sY + (MODE == 0 ? (int64_t)e * a.sy_estride : 0) + j0 * 4;
+  L.x_bytes = rows_x * a.ldx;
+  L.y_bytes = rows_y * a.ldx;
+  L.sx_rows4 = (a.I - i0) * 4;     // rows past a group end hold a neighbour's (finite) scales
+  L.sy_rows4 = (a.J - j0) * 4;
+  L.nchunks = a.Kc / kBK;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int row = (wv * 8 + u) * 8 + (lane >> 3);
+    L.voff[u] = row * (int)a.ldx + (((lane & 7) ^ piece_swz(row)) << 4);
+  }
 
   v16f acc[4][4];
 #pragma unroll
@@ -247,103 +356,167 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = (v16f){};
 
-  const int64_t klen = td.k1 - td.k0;
-  const int nk = (int)((klen + kBK - 1) / kBK);
-  // scale-row base: sY rows for this tile start at j0
-  const uint8_t* sYt = sYg + sy_row0 * a.ldsy;
-  const int64_t sy_total_t = sy_total - sy_row0 * a.ldsy;
-
-  if (nk > 0) {
-    issue_stage(smem, Xg, sXg, Yg, sYt, x_rows_lo, x_rows_hi, y_rows_hi, a.ldx, a.ldsx, a.ldy, a.ldsy, sx_total,
-                sy_total_t, td.k0, td.k0, td.k1);
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_vmcnt0();
-    __syncthreads();
-    const int64_t kk = td.k0 + (int64_t)kt * kBK;
-    if (kt + 1 < nk) {
-      issue_stage(smem + ((kt + 1) & 1) * kStageBytes, Xg, sXg, Yg, sYt, x_rows_lo, x_rows_hi, y_rows_hi, a.ldx,
-                  a.ldsx, a.ldy, a.ldsy, sx_total, sy_total_t, kk + kBK, td.k0, td.k1);
-    }
-    const uint8_t* st = smem + (kt & 1) * kStageBytes;
-    const uint8_t* xs = st;
-    const uint8_t* ys = st + kTileBytes;
-    const uint8_t* sxs = st + 2 * kTileBytes;
-    const uint8_t* sys = sxs + kScaleBytes;
-    // number of valid 32-blocks in this stage (1..4)
-    const int64_t rem = td.k1 - kk;
-    const int nvalid = rem >= kBK ? 4 : (int)(rem >> 5);
-    // byte offset of block kk/32 inside each row's staged dword pair
-    const int64_t kb = kk >> 5;
+  const int ns = (int)((k1 - k0 + kBK - 1) / kBK);
+  if (ns > 0) {
+    // this lane's rows and piece offsets (the swizzle depends only on l32)
+    const int sw = piece_swz(l32);
+    int pc[2][2];   // [window][chunk] byte offset of the piece inside a row
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      v8i yf[4], xf[4];
-      int ysc[4], xsc[4];
+    for (int w = 0; w < 2; ++w)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) pc[w][c] = ((4 * w + half + 2 * c) ^ sw) << 4;
+    const int yrow0 = jw * 128 + l32, xrow0 = iw * 128 + l32;
+    Frag X[4], Y[4];
+
+    // DMA issue is spread one load per MFMA: loads 0..11 of stage s+2 follow
+    // the 12 MFMAs after stage s's barrier, loads 12..16 the first 5 MFMAs
+    // of stage s+1, all before stage s+1's barrier waits for them.
+    {
+      const StageDma d0 = make_stage_dma(smem, 0, L, k0, 0, ns, wv);
+      issue_loads<0, 17>(d0, L, wv, lane);
+    }
+    StageDma pend = make_stage_dma(smem, 1, L, k0, 1, ns, wv);
+    issue_loads<0, 12>(pend, L, wv, lane);
+    first_barrier();   // stage 0 has landed
+    {
+      const uint8_t* st = smem;
+      const int soff = (int)((k0 >> 5) & 3);
+      const int nvalid = (int)min((int64_t)4, (k1 - k0) >> 5);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int yrow = jw * 128 + q * 32 + l32;
-        const int xrow = iw * 128 + q * 32 + l32;
-        // pieces 4s + half and 4s + half + 2 of the row
-        const int p0 = 4 * s + half, p1 = p0 + 2;
-        const v4i y0 = *(const v4i*)(ys + yrow * kBK + ((p0 ^ piece_swz(yrow)) << 4));
-        const v4i y1 = *(const v4i*)(ys + yrow * kBK + ((p1 ^ piece_swz(yrow)) << 4));
-        const v4i x0 = *(const v4i*)(xs + xrow * kBK + ((p0 ^ piece_swz(xrow)) << 4));
-        const v4i x1 = *(const v4i*)(xs + xrow * kBK + ((p1 ^ piece_swz(xrow)) << 4));
-        yf[q] = (v8i){y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
-        xf[q] = (v8i){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        // scale byte of block 2s + half for this row
-        int64_t yr = yrow;
-        if (yr > y_rows_hi) yr = y_rows_hi;
-        int64_t xr = x_rows_lo + xrow;
-        if (xr > x_rows_hi) xr = x_rows_hi;
-        const int yoff = (int)(((yr)*a.ldsy + kb) & 3) + 2 * s + half;
-        const int xoff = (int)((xr * a.ldsx + kb) & 3) + 2 * s + half;
-        ysc[q] = sys[yrow * 8 + yoff];
-        xsc[q] = sxs[xrow * 8 + xoff];
+        read_frag<MODE == 1>(st + kTileBytes, st + 2 * kTileBytes + 2 * kScaleChunk, yrow0 + q * 32, pc[0][0],
+                             pc[0][1], 0, half, soff, nvalid, Y[q]);
+        read_frag<MODE == 1>(st, st + 2 * kTileBytes, xrow0 + q * 32, pc[0][0], pc[0][1], 0, half, soff, nvalid,
+                             X[q]);
       }
-      if (nvalid < 4) {
-        // blocks 2s and 2s+1 of the stage; chunk c of each lane lies in block 2s + c,
-        // the lane's scale covers block 2s + half
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            if (2 * s + c >= nvalid) {
-#pragma unroll
-              for (int v = 0; v < 4; ++v) {
-                yf[q][4 * c + v] = 0;
-                xf[q][4 * c + v] = 0;
-              }
-            }
-          }
-          if (2 * s + half >= nvalid) {
-            ysc[q] = 127;
-            xsc[q] = 127;
-          }
-        }
-      }
-#pragma unroll
-      for (int qy = 0; qy < 4; ++qy)
-#pragma unroll
-        for (int qx = 0; qx < 4; ++qx)
-          acc[qy][qx] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(yf[qy], xf[qx], acc[qy][qx], 0, 0, 0,
-                                                                        ysc[qy], 0, xsc[qx]);
     }
+    for (int kt = 0; kt < ns; ++kt) {
+      const int buf = kt & 1;
+      const uint8_t* cs = smem + buf * kStageBytes;           // this stage
+      const uint8_t* nst = smem + (buf ^ 1) * kStageBytes;    // next stage
+      const int64_t kk = k0 + (int64_t)kt * kBK;
+      const int soff = (int)((kk >> 5) & 3);
+      const int nvalid = (int)min((int64_t)4, (k1 - kk) >> 5);
+      const int64_t kn = kk + kBK;
+      const int soff_n = (int)((kn >> 5) & 3);
+      const int nvalid_n = (int)min((int64_t)4, max((k1 - kn) >> 5, (int64_t)0));
+
+      // ---- window 0 of stage kt; refill with window 1 of stage kt; finish
+      // ---- the DMA of stage kt+1 (loads 12..16) ----
+      acc[0][0] = mfma(Y[0], X[0], acc[0][0]);
+      issue_load<12>(pend, L, wv, lane);
+      MX_FENCE();
+      acc[1][0] = mfma(Y[1], X[0], acc[1][0]);
+      issue_load<13>(pend, L, wv, lane);
+      MX_FENCE();
+      acc[2][0] = mfma(Y[2], X[0], acc[2][0]);
+      issue_load<14>(pend, L, wv, lane);
+      MX_FENCE();
+      acc[3][0] = mfma(Y[3], X[0], acc[3][0]);
+      issue_load<15>(pend, L, wv, lane);
+      MX_FENCE();
+      read_frag<MODE == 1>(cs, cs + 2 * kTileBytes, xrow0, pc[1][0], pc[1][1], 1, half, soff, nvalid, X[0]);
+      MX_FENCE();
+      acc[0][1] = mfma(Y[0], X[1], acc[0][1]);
+      issue_load<16>(pend, L, wv, lane);
+      MX_FENCE();
+#pragma unroll
+      for (int qy = 1; qy < 4; ++qy) acc[qy][1] = mfma(Y[qy], X[1], acc[qy][1]);
+      read_frag<MODE == 1>(cs, cs + 2 * kTileBytes, xrow0 + 32, pc[1][0], pc[1][1], 1, half, soff, nvalid, X[1]);
+      MX_FENCE();
+#pragma unroll
+      for (int qy = 0; qy < 4; ++qy) acc[qy][2] = mfma(Y[qy], X[2], acc[qy][2]);
+      read_frag<MODE == 1>(cs, cs + 2 * kTileBytes, xrow0 + 64, pc[1][0], pc[1][1], 1, half, soff, nvalid, X[2]);
+      MX_FENCE();
+#pragma unroll
+      for (int qy = 0; qy < 4; ++qy) {
+        acc[qy][3] = mfma(Y[qy], X[3], acc[qy][3]);
+        read_frag<MODE == 1>(cs + kTileBytes, cs + 2 * kTileBytes + 2 * kScaleChunk, yrow0 + qy * 32, pc[1][0],
+                             pc[1][1], 1, half, soff, nvalid, Y[qy]);
+      }
+      read_frag<MODE == 1>(cs, cs + 2 * kTileBytes, xrow0 + 96, pc[1][0], pc[1][1], 1, half, soff, nvalid, X[3]);
+      MX_FENCE();
+
+      // ---- window 1 of stage kt; refill with window 0 of stage kt+1; start
+      // ---- the DMA of stage kt+2 into this buffer (loads 0..11) ----
+#pragma unroll
+      for (int qy = 0; qy < 4; ++qy) acc[qy][0] = mfma(Y[qy], X[0], acc[qy][0]);
+      MX_FENCE();
+      stage_barrier();   // stage kt+1 landed; every wave is done reading buffer `buf`
+      pend = make_stage_dma(smem, buf, L, k0, kt + 2, ns, wv);
+      read_frag<MODE == 1>(nst, nst + 2 * kTileBytes, xrow0, pc[0][0], pc[0][1], 0, half, soff_n, nvalid_n, X[0]);
+      MX_FENCE();
+      acc[0][1] = mfma(Y[0], X[1], acc[0][1]);
+      issue_load<0>(pend, L, wv, lane);
+      MX_FENCE();
+      acc[1][1] = mfma(Y[1], X[1], acc[1][1]);
+      issue_load<1>(pend, L, wv, lane);
+      MX_FENCE();
+      acc[2][1] = mfma(Y[2], X[1], acc[2][1]);
+      issue_load<2>(pend, L, wv, lane);
+      MX_FENCE();
+      acc[3][1] = mfma(Y[3], X[1], acc[3][1]);
+      issue_load<3>(pend, L, wv, lane);
+      MX_FENCE();
+      read_frag<MODE == 1>(nst, nst + 2 * kTileBytes, xrow0 + 32, pc[0][0], pc[0][1], 0, half, soff_n, nvalid_n,
+                           X[1]);
+      MX_FENCE();
+      acc[0][2] = mfma(Y[0], X[2], acc[0][2]);
+      issue_load<4>(pend, L, wv, lane);
+      MX_FENCE();
+      acc[1][2] = mfma(Y[1], X[2], acc[1][2]);
+      issue_load<5>(pend, L, wv, lane);
+      MX_FENCE();
+      acc[2][2] = mfma(Y[2], X[2], acc[2][2]);
+      issue_load<6>(pend, L, wv, lane);
+      MX_FENCE();
+      acc[3][2] = mfma(Y[3], X[2], acc[3][2]);
+      issue_load<7>(pend, L, wv, lane);
+      MX_FENCE();
+      read_frag<MODE == 1>(nst, nst + 2 * kTileBytes, xrow0 + 64, pc[0][0], pc[0][1], 0, half, soff_n, nvalid_n,
+                           X[2]);
+      MX_FENCE();
+      acc[0][3] = mfma(Y[0], X[3], acc[0][3]);
+      issue_load<8>(pend, L, wv, lane);
+      MX_FENCE();
+      read_frag<MODE == 1>(nst + kTileBytes, nst + 2 * kTileBytes + 2 * kScaleChunk, yrow0, pc[0][0], pc[0][1], 0,
+                           half, soff_n, nvalid_n, Y[0]);
+      acc[1][3] = mfma(Y[1], X[3], acc[1][3]);
+      issue_load<9>(pend, L, wv, lane);
+      MX_FENCE();
+      read_frag<MODE == 1>(nst + kTileBytes, nst + 2 * kTileBytes + 2 * kScaleChunk, yrow0 + 32, pc[0][0],
+                           pc[0][1], 0, half, soff_n, nvalid_n, Y[1]);
+      acc[2][3] = mfma(Y[2], X[3], acc[2][3]);
+      issue_load<10>(pend, L, wv, lane);
+      MX_FENCE();
+      read_frag<MODE == 1>(nst + kTileBytes, nst + 2 * kTileBytes + 2 * kScaleChunk, yrow0 + 64, pc[0][0],
+                           pc[0][1], 0, half, soff_n, nvalid_n, Y[2]);
+      acc[3][3] = mfma(Y[3], X[3], acc[3][3]);
+      issue_load<11>(pend, L, wv, lane);
+      MX_FENCE();
+      read_frag<MODE == 1>(nst + kTileBytes, nst + 2 * kTileBytes + 2 * kScaleChunk, yrow0 + 96, pc[0][0],
+                           pc[0][1], 0, half, soff_n, nvalid_n, Y[3]);
+      read_frag<MODE == 1>(nst, nst + 2 * kTileBytes, xrow0 + 96, pc[0][0], pc[0][1], 0, half, soff_n, nvalid_n,
+                           X[3]);
+      MX_FENCE();
+    }
+    // drain the empty-range loads still in flight before the workgroup ends
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
   // epilogue: lane holds output row i = i0 + iw*128 + qx*32 + l32 and, for
   // register group g, columns j0 + jw*128 + qy*32 + 8g + 4*half + 0..3.
-  const int64_t c_off = MODE == 1 ? (int64_t)td.e * a.c_estride : 0;
-  const int64_t i_lim = MODE == 0 ? td.i_end : a.I;
+  const int64_t c_off = MODE == 1 ? (int64_t)e * a.c_estride : 0;
+  const int64_t i_lim = x_end;
 #pragma unroll
   for (int qx = 0; qx < 4; ++qx) {
-    const int64_t i = td.i0 + iw * 128 + qx * 32 + l32;
+    const int64_t i = i0 + iw * 128 + qx * 32 + l32;
     if (i >= i_lim) continue;
 #pragma unroll
     for (int qy = 0; qy < 4; ++qy) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int64_t j = td.j0 + jw * 128 + qy * 32 + 8 * g + 4 * half;
+        const int64_t j = j0 + jw * 128 + qy * 32 + 8 * g + 4 * half;
         if (j < a.J) {
           const v16f& v = acc[qy][qx];
           if (OUT_F32) {
@@ -358,6 +531,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
           }
         }
       }
+      // one 32x32 tile at a time: keeps the accumulator reads from being
+      // hoisted all at once (register pressure)
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }

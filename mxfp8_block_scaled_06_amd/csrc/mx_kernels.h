@@ -19,20 +19,22 @@ struct GemmArgs {
   int64_t I, J, Kc;
   int E;
   int mode;
-  int64_t ldx, ldsx;          // bytes per row of X and of its scales
-  int64_t ldy, ldsy;          // bytes per row of Y and of its scales
+  int64_t ldx;                // bytes per row of X and of Y (== Kc)
   int64_t y_estride;          // mode 0: bytes between experts of Y
   int64_t sy_estride;         // mode 0: bytes between experts of sY
-  int64_t sx_total;           // bytes of the sX tensor
-  int64_t sy_total_per_e;     // bytes of one expert's sY (mode 0) / of sY (mode 1)
   int64_t ldc;                // elements per row of C
   int64_t c_estride;          // mode 1: elements between experts of C
 };
 
+// gemm_rows_per_batch == 0: row-major scales [rows_total][cols/32]; > 0:
+// GEMM scale layout [rows_total/R][cols/128][R][4] with R = gemm_rows_per_batch.
 hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows_total, int64_t cols, uint8_t* q, uint8_t* s,
-                                hipStream_t st);
+                                int64_t gemm_rows_per_batch, hipStream_t st);
+// gemm_layout == 0: s_t [batch][cols][lds]; 1: GEMM layout [batch][ldq/128][cols][4].
 hipError_t launch_quant_colwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q_t,
-                                int64_t ldq, uint8_t* s_t, int64_t lds, hipStream_t st);
+                                int64_t ldq, uint8_t* s_t, int64_t lds, int gemm_layout, hipStream_t st);
+hipError_t launch_scales_to_gemm(const uint8_t* s, int64_t batch, int64_t rows, int64_t kb, uint8_t* out,
+                                 hipStream_t st);
 hipError_t launch_quant_32x32(const uint16_t* x, int64_t rows_total, int64_t cols, uint8_t* q, uint8_t* s,
                               hipStream_t st);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t st);

@@ -29,10 +29,23 @@ namespace mxk {
 constexpr int kRowThreads = 256;
 constexpr int kRowU = 4;
 
+// Scale byte destination.  Row-major: block g (row-major over rows x KB
+// blocks) goes to s[g].  GEMM layout (rows_per_batch > 0): [batch][KB/4]
+// [rows_per_batch][4], so the 4 blocks of a 128-wide contraction step of 256
+// consecutive rows form one contiguous 1 KiB run for the GEMM's loads.
+__device__ __forceinline__ uint32_t row_scale_index(uint32_t g, uint32_t kb_per_row, uint32_t rows_per_batch) {
+  if (rows_per_batch == 0) return g;
+  const uint32_t r = g / kb_per_row, kb = g - r * kb_per_row;
+  const uint32_t b = r / rows_per_batch, rr = r - b * rows_per_batch;
+  return b * kb_per_row * rows_per_batch + (kb >> 2) * rows_per_batch * 4 + rr * 4 + (kb & 3);
+}
+
 __global__ __launch_bounds__(kRowThreads) void quant_rowwise_kernel(const uint16_t* __restrict__ x,
                                                                     int64_t nchunks,
                                                                     uint8_t* __restrict__ q,
-                                                                    uint8_t* __restrict__ s) {
+                                                                    uint8_t* __restrict__ s,
+                                                                    uint32_t kb_per_row,
+                                                                    uint32_t rows_per_batch) {
   const int64_t base = (int64_t)blockIdx.x * (kRowThreads * kRowU) + threadIdx.x;
   v4i w[kRowU];
 #pragma unroll
@@ -59,7 +72,7 @@ __global__ __launch_bounds__(kRowThreads) void quant_rowwise_kernel(const uint16
         codes = quant8(w[u], inv_scale_from_e8m0(byte));
       }
       *(v2i*)(q + idx * 8) = codes;
-      if ((threadIdx.x & 3) == 0) s[idx >> 2] = (uint8_t)byte;
+      if ((threadIdx.x & 3) == 0) s[row_scale_index((uint32_t)(idx >> 2), kb_per_row, rows_per_batch)] = (uint8_t)byte;
     }
   }
 }
@@ -77,7 +90,7 @@ constexpr int kColTile = 128;
 __global__ __launch_bounds__(256) void quant_colwise_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                             int64_t cols, uint8_t* __restrict__ q_t,
                                                             int64_t ldq, uint8_t* __restrict__ s_t,
-                                                            int64_t lds) {
+                                                            int64_t lds, int gemm_layout) {
   __shared__ v4i tile[kColTile * (kColTile / 8)];  // [128 rows][16 chunks of 8 bf16]
   const int tid = threadIdx.x;
   const int64_t b = blockIdx.z;
@@ -130,9 +143,17 @@ __global__ __launch_bounds__(256) void quant_colwise_kernel(const uint16_t* __re
   *(v4i*)(q0 + 16) = out0[1];
   *(v4i*)(q1) = out1[0];
   *(v4i*)(q1 + 16) = out1[1];
-  uint8_t* sp = s_t + (b * cols + col) * lds + (rb >> 5);
-  sp[0] = (uint8_t)byte0;
-  sp[lds] = (uint8_t)byte1;
+  if (gemm_layout) {
+    // [batch][ldq/128][cols][4]: block rb/32 of output row `col`
+    const int64_t blk = rb >> 5;
+    uint8_t* sp = s_t + b * (ldq / 32) * cols + (blk >> 2) * cols * 4 + col * 4 + (blk & 3);
+    sp[0] = (uint8_t)byte0;
+    sp[4] = (uint8_t)byte1;
+  } else {
+    uint8_t* sp = s_t + (b * cols + col) * lds + (rb >> 5);
+    sp[0] = (uint8_t)byte0;
+    sp[lds] = (uint8_t)byte1;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -177,21 +198,47 @@ __global__ __launch_bounds__(256) void quant_32x32_kernel(const uint16_t* __rest
 // Launchers (sizes validated by the caller).
 // ---------------------------------------------------------------------------
 hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows_total, int64_t cols, uint8_t* q, uint8_t* s,
-                                hipStream_t st) {
+                                int64_t gemm_rows_per_batch, hipStream_t st) {
   const int64_t nchunks = rows_total * (cols / 8);
   if (nchunks == 0) return hipSuccess;
   const int64_t per_block = (int64_t)kRowThreads * kRowU;
   const int64_t grid = (nchunks + per_block - 1) / per_block;
-  hipLaunchKernelGGL(quant_rowwise_kernel, dim3((unsigned)grid), dim3(kRowThreads), 0, st, x, nchunks, q, s);
+  hipLaunchKernelGGL(quant_rowwise_kernel, dim3((unsigned)grid), dim3(kRowThreads), 0, st, x, nchunks, q, s,
+                     (uint32_t)(cols / 32), (uint32_t)gemm_rows_per_batch);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_colwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q_t,
-                                int64_t ldq, uint8_t* s_t, int64_t lds, hipStream_t st) {
+                                int64_t ldq, uint8_t* s_t, int64_t lds, int gemm_layout, hipStream_t st) {
   if (batch == 0 || rows == 0 || cols == 0) return hipSuccess;
   dim3 grid((unsigned)((cols + kColTile - 1) / kColTile), (unsigned)((rows + kColTile - 1) / kColTile),
             (unsigned)batch);
-  hipLaunchKernelGGL(quant_colwise_kernel, grid, dim3(256), 0, st, x, rows, cols, q_t, ldq, s_t, lds);
+  hipLaunchKernelGGL(quant_colwise_kernel, grid, dim3(256), 0, st, x, rows, cols, q_t, ldq, s_t, lds, gemm_layout);
+  return hipGetLastError();
+}
+
+// Row-major scales [batch][rows][kb] -> GEMM layout [batch][kb/4][rows][4]
+// (kb % 4 == 0).  One thread per output dword (4 scale bytes).
+__global__ __launch_bounds__(256) void scales_to_gemm_kernel(const uint8_t* __restrict__ s, int64_t batch,
+                                                             int64_t rows, int64_t kb, uint8_t* __restrict__ out) {
+  const int64_t n = batch * rows * (kb / 4);
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  // output dword i = (b, c, r): c = chunk of 4 blocks
+  const int64_t per_b = rows * (kb / 4);
+  const int64_t b = i / per_b, rem = i - b * per_b;
+  const int64_t c = rem / rows, r = rem - c * rows;
+  const uint8_t* src = s + (b * rows + r) * kb + 4 * c;
+  const uint32_t w = (uint32_t)src[0] | ((uint32_t)src[1] << 8) | ((uint32_t)src[2] << 16) | ((uint32_t)src[3] << 24);
+  *(uint32_t*)(out + 4 * i) = w;
+}
+
+hipError_t launch_scales_to_gemm(const uint8_t* s, int64_t batch, int64_t rows, int64_t kb, uint8_t* out,
+                                 hipStream_t st) {
+  const int64_t n = batch * rows * (kb / 4);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(scales_to_gemm_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, s, batch, rows, kb,
+                     out);
   return hipGetLastError();
 }
 

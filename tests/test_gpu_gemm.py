@@ -138,7 +138,9 @@ def test_gemm_mx_random_operands(mode):
         sY = rng.integers(112, 142, size=(J, Kc // 32)).astype(np.uint8)
     offs = inp.offsets_from_counts(counts)
     log(f"gemm_mx mode={mode} counts={counts}")
-    args = (to_dev_u8(X), to_dev_u8(sX), to_dev_u8(Y), to_dev_u8(sY), to_dev_i32(offs), mode)
+    gX = mx.mx_scales_to_gemm_layout(to_dev_u8(sX))
+    gY = mx.mx_scales_to_gemm_layout(to_dev_u8(sY))
+    args = (to_dev_u8(X), gX, to_dev_u8(Y), gY, to_dev_i32(offs), mode)
     C = bf16_host_bits(mx.mx_grouped_gemm_mx(*args))
     C32 = mx.mx_grouped_gemm_mx_f32(*args).cpu().numpy()
     ref = oracle.grouped_gemm_mx(X, sX, Y, sY, offs, mode)
@@ -147,6 +149,18 @@ def test_gemm_mx_random_operands(mode):
     _r1(C32, ref, f"gemm_mx_f32 mode {mode}", absd, f32=True)
     # the bf16 epilogue is exactly round-to-nearest-even of the fp32 accumulators
     np.testing.assert_array_equal(C, inp.f32_to_bf16_bits(C32.astype(np.float32)))
+
+
+@pytest.mark.parametrize("shape", [(1, 64, 8), (3, 100, 12), (2, 256, 160)])
+def test_scales_to_gemm_layout_is_the_blocked_permutation(shape):
+    """Integer permutation, bit-exact: (b, r, kb) -> [b][kb/4][r][kb%4]."""
+    require_gpu()
+    import mxfp8_block_scaled_06_amd as mx
+    s = np.random.default_rng(shape[1]).integers(0, 256, size=shape, dtype=np.int64).astype(np.uint8)
+    B, R, KB = shape
+    want = s.reshape(B, R, KB // 4, 4).transpose(0, 2, 1, 3)
+    got = mx.mx_scales_to_gemm_layout(to_dev_u8(s)).cpu().numpy().reshape(B, KB // 4, R, 4)
+    np.testing.assert_array_equal(got, want)
 
 
 def test_gemm_deterministic_and_errors():
