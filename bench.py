@@ -89,9 +89,10 @@ def traffic_for_current_kernel():
         return None
 
 
-def cpu_baseline(x, budget_rows=96):
-    """The oracle, as it stands, on a bounded sample of the forward: one expert's
-    weights quantized and `budget_rows` of its tokens multiplied in fp64."""
+def cpu_baseline(x, experts=8, rows_per_expert=128):
+    """The oracle, as it stands, on a bounded sample of the forward: for
+    `experts` experts, quantize the expert's weights and multiply
+    `rows_per_expert` of its tokens in fp64 (numpy BLAS on every core)."""
     import numpy as np
     import oracle
     try:
@@ -100,19 +101,22 @@ def cpu_baseline(x, budget_rows=96):
     except Exception:
         threads = os.cpu_count()
     bounds = oracle.group_bounds(x.offs, x.M_rows)
-    e = int(np.argmax([b - a for a, b in bounds]))
-    a, _ = bounds[e]
-    rows = np.arange(a, a + budget_rows)
+    order = np.argsort([-(b - a) for a, b in bounds])[:experts]
+    flops = 0.0
     t0 = time.perf_counter()
-    qW, sW = oracle.quantize_rowwise(x.W[e])
-    qA, sA = oracle.quantize_rowwise(x.A[rows])
-    out = oracle.dequant_rowwise(qA, sA) @ oracle.dequant_rowwise(qW, sW).T
+    for e in order:
+        a, b = bounds[int(e)]
+        rows = np.arange(a, min(b, a + rows_per_expert))
+        qW, sW = oracle.quantize_rowwise(x.W[int(e)])
+        qA, sA = oracle.quantize_rowwise(x.A[rows])
+        out = oracle.dequant_rowwise(qA, sA) @ oracle.dequant_rowwise(qW, sW).T
+        flops += 2.0 * len(rows) * x.W.shape[1] * x.W.shape[2]
+        assert out.shape == (len(rows), x.W.shape[1])
     dt = time.perf_counter() - t0
-    flops = 2.0 * budget_rows * x.W.shape[1] * x.W.shape[2]
-    assert out.shape == (budget_rows, x.W.shape[1])
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"forward of {budget_rows} tokens of expert {e} incl. quantizing that expert's "
-                      f"[{x.W.shape[1]}, {x.W.shape[2]}] weights (fp64 numpy); {dt:.1f} s",
+            "sample": f"forward of {rows_per_expert} tokens for each of {len(order)} experts, including "
+                      f"quantizing those experts' [{x.W.shape[1]}, {x.W.shape[2]}] weights (fp64 numpy); "
+                      f"{dt:.1f} s",
             "seconds": dt}
 
 
