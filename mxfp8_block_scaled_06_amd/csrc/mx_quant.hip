@@ -24,10 +24,11 @@ namespace mxk {
 // Rowwise: x viewed as [rows, cols] (batch folded into rows), dense outputs.
 // One 16-byte chunk (8 values) per lane and load; a DPP quad holds one block.
 // Each thread handles kRowU chunks spaced by the block size so every wave-wide
-// load instruction reads 1 KiB of contiguous input.
+// load instruction reads 1 KiB of contiguous input (two chunks per thread
+// measured fastest: more waves in flight, shorter per-wave tails).
 // ---------------------------------------------------------------------------
 constexpr int kRowThreads = 256;
-constexpr int kRowU = 4;
+constexpr int kRowU = 2;
 
 // Scale byte destination.  Row-major: block g (row-major over rows x KB
 // blocks) goes to s[g].  GEMM layout (rows_per_batch > 0): [batch][KB/4]
@@ -78,20 +79,24 @@ __global__ __launch_bounds__(kRowThreads) void quant_rowwise_kernel(const uint16
 }
 
 // ---------------------------------------------------------------------------
-// Colwise: x [batch, rows, cols] -> q_t [batch, cols, ldq], s_t [batch, cols, lds]
-// (ldq >= rows, lds >= rows/32).  A workgroup stages a 128x128 bf16 tile in
-// LDS (coalesced 256-byte row segments), then wave w quantizes rows
-// [32w, 32w+32) of the tile: lane l owns columns 2l and 2l+1, reads its 32
-// dwords conflict-free (one LDS row per step), and writes two 32-byte runs of
-// the transposed output.
+// Colwise: x [batch, rows, cols] -> q_t [batch, cols, ldq], s_t (ldq >= rows).
+// A workgroup stages a 128x128 bf16 tile in LDS (coalesced 256-byte row
+// segments); wave w quantizes rows [32w, 32w+32) of the tile: lane l owns
+// columns 2l and 2l+1 and reads its 32 dwords conflict-free (one LDS row per
+// step).  The codes go back through the same LDS buffer, transposed, so every
+// global store instruction writes whole 128-byte lines of q_t (8 lanes per
+// output row) instead of 32-byte pieces of 64 different rows.
 // ---------------------------------------------------------------------------
 constexpr int kColTile = 128;
+constexpr int kColPitch = 144;   // bytes per staged output row (128 codes + 16 pad)
+
+static_assert(kColTile * kColPitch + kColTile * 4 <= kColTile * kColTile * 2, "codes and scales fit the input tile");
 
 __global__ __launch_bounds__(256) void quant_colwise_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                             int64_t cols, uint8_t* __restrict__ q_t,
                                                             int64_t ldq, uint8_t* __restrict__ s_t,
                                                             int64_t lds, int gemm_layout) {
-  __shared__ v4i tile[kColTile * (kColTile / 8)];  // [128 rows][16 chunks of 8 bf16]
+  __shared__ v4i tile[kColTile * (kColTile / 8)];  // [128 rows][16 chunks of 8 bf16], later the codes
   const int tid = threadIdx.x;
   const int64_t b = blockIdx.z;
   const int64_t r0 = (int64_t)blockIdx.y * kColTile;
@@ -108,9 +113,6 @@ __global__ __launch_bounds__(256) void quant_colwise_kernel(const uint16_t* __re
   }
   __syncthreads();
   const int wv = tid >> 6, lane = tid & 63;
-  const int64_t rb = r0 + 32 * wv;     // first row of this wave's block
-  const int64_t col = c0 + 2 * lane;   // even; cols % 8 == 0 so col+1 is valid too
-  if (rb >= rows || col >= cols) return;
   const uint32_t* t32 = (const uint32_t*)tile;
   uint32_t v[32];
   uint32_t am0 = 0, am1 = 0;
@@ -137,61 +139,86 @@ __global__ __launch_bounds__(256) void quant_colwise_kernel(const uint16_t* __re
       out1[h][d] = byte1 == 0xFFu ? 0x7F7F7F7F : c;
     }
   }
-  uint8_t* q0 = q_t + (b * cols + col) * ldq + rb;
-  uint8_t* q1 = q0 + ldq;
-  *(v4i*)(q0) = out0[0];
-  *(v4i*)(q0 + 16) = out0[1];
-  *(v4i*)(q1) = out1[0];
-  *(v4i*)(q1 + 16) = out1[1];
-  if (gemm_layout) {
-    // [batch][ldq/128][cols][4]: block rb/32 of output row `col`
-    const int64_t blk = rb >> 5;
-    uint8_t* sp = s_t + b * (ldq / 32) * cols + (blk >> 2) * cols * 4 + col * 4 + (blk & 3);
-    sp[0] = (uint8_t)byte0;
-    sp[4] = (uint8_t)byte1;
-  } else {
-    uint8_t* sp = s_t + (b * cols + col) * lds + (rb >> 5);
-    sp[0] = (uint8_t)byte0;
-    sp[lds] = (uint8_t)byte1;
+  __syncthreads();   // every wave has its input in registers: the tile becomes the output stage
+  uint8_t* o8 = (uint8_t*)tile;
+  uint8_t* sc = o8 + kColTile * kColPitch;   // [128 output rows][4 blocks]
+  *(v4i*)(o8 + (2 * lane) * kColPitch + 32 * wv) = out0[0];
+  *(v4i*)(o8 + (2 * lane) * kColPitch + 32 * wv + 16) = out0[1];
+  *(v4i*)(o8 + (2 * lane + 1) * kColPitch + 32 * wv) = out1[0];
+  *(v4i*)(o8 + (2 * lane + 1) * kColPitch + 32 * wv + 16) = out1[1];
+  sc[(2 * lane) * 4 + wv] = (uint8_t)byte0;
+  sc[(2 * lane + 1) * 4 + wv] = (uint8_t)byte1;
+  __syncthreads();
+  // 128 output rows x 8 pieces of 16 bytes; 8 consecutive lanes fill one line
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int p = j * 256 + tid;
+    const int orow = p >> 3, pc = p & 7;
+    const int64_t col = c0 + orow, rr = r0 + 16 * pc;
+    if (col < cols && rr < rows) {
+      const v4i w = *(const v4i*)(o8 + orow * kColPitch + 16 * pc);
+      *(v4i*)(q_t + (b * cols + col) * ldq + rr) = w;
+    }
+  }
+  // scales: thread t < 128 owns output row c0 + t and its (up to) 4 blocks
+  if (tid < kColTile) {
+    const int64_t col = c0 + tid;
+    const int64_t nblk = min((int64_t)4, (rows - r0) >> 5);   // rows % 32 == 0
+    if (col < cols) {
+      const uint32_t w4 = *(const uint32_t*)(sc + tid * 4);
+      if (gemm_layout) {
+        // [batch][ldq/128][cols][4]: blocks r0/32 .. r0/32+3 of output row `col` (r0 % 128 == 0)
+        uint8_t* sp = s_t + b * (ldq / 32) * cols + (r0 >> 7) * cols * 4 + col * 4;
+        if (nblk == 4) {
+          *(uint32_t*)sp = w4;
+        } else {
+          for (int k = 0; k < nblk; ++k) sp[k] = (uint8_t)(w4 >> (8 * k));
+        }
+      } else {
+        uint8_t* sp = s_t + (b * cols + col) * lds + (r0 >> 5);
+        for (int k = 0; k < nblk; ++k) sp[k] = (uint8_t)(w4 >> (8 * k));
+      }
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // 32x32: x viewed as [rows, cols] (batch folded into rows; rows % 32 == 0).
-// A workgroup covers 32 rows x 256 columns; wave w covers columns
-// [64w, 64w+64) = two 32x32 tiles.  Lane l holds 8 columns (chunk l%8) of rows
-// l/8 + 8u, u = 0..3.  The tile amax is a wave reduction over the 32 lanes
-// sharing bit 2 of the lane id (DPP quad max, then xor-shuffles 8/16/32).
+// A workgroup covers 32 rows x 512 columns; wave w covers columns
+// [128w, 128w+128) = four 32x32 tiles.  Lane l holds 8 columns (chunk l%16) of
+// rows l/16 + 4u, u = 0..7, so every load and store instruction moves whole
+// lines (16 lanes per row).  The tile amax is a wave reduction over the 16
+// lanes of one tile: DPP quad max (the tile's four chunks), then
+// xor-shuffles 16/32 (its four row groups).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void quant_32x32_kernel(const uint16_t* __restrict__ x, int64_t cols,
                                                           uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int64_t r0 = (int64_t)blockIdx.y * 32;
-  const int64_t col = (int64_t)blockIdx.x * 256 + wv * 64 + (lane & 7) * 8;
-  const bool valid = col < cols;  // cols % 32 == 0: whole tiles are valid or not
-  v4i w[4];
+  const int64_t col = (int64_t)blockIdx.x * 512 + wv * 128 + (lane & 15) * 8;
+  const bool valid = col < cols;
+  v4i w[8];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t row = r0 + (lane >> 3) + 8 * u;
+  for (int u = 0; u < 8; ++u) {
+    const int64_t row = r0 + (lane >> 4) + 4 * u;
     w[u] = valid ? __builtin_nontemporal_load((const v4i*)(x + row * cols + col)) : (v4i){0, 0, 0, 0};
   }
   uint32_t am = 0;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) am = max(am, absmax8(w[u]));
+  for (int u = 0; u < 8; ++u) am = max(am, absmax8(w[u]));
   am = quad_max(am);
-  am = max(am, (uint32_t)__shfl_xor((int)am, 8));
   am = max(am, (uint32_t)__shfl_xor((int)am, 16));
   am = max(am, (uint32_t)__shfl_xor((int)am, 32));
   if (!valid) return;
   const uint32_t byte = e8m0_from_absbits(am);
   const float m = inv_scale_from_e8m0(byte == 0xFFu ? 127u : byte);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t row = r0 + (lane >> 3) + 8 * u;
+  for (int u = 0; u < 8; ++u) {
+    const int64_t row = r0 + (lane >> 4) + 4 * u;
     v2i codes = byte == 0xFFu ? (v2i){0x7F7F7F7F, 0x7F7F7F7F} : quant8(w[u], m);
     *(v2i*)(q + row * cols + col) = codes;
   }
-  if ((lane & 3) == 0 && (lane >> 3) == 0) s[(r0 >> 5) * (cols >> 5) + (col >> 5)] = (uint8_t)byte;
+  if ((lane & 3) == 0 && (lane >> 4) == 0) s[(r0 >> 5) * (cols >> 5) + (col >> 5)] = (uint8_t)byte;
 }
 
 // ---------------------------------------------------------------------------
@@ -245,7 +272,7 @@ hipError_t launch_scales_to_gemm(const uint8_t* s, int64_t batch, int64_t rows, 
 hipError_t launch_quant_32x32(const uint16_t* x, int64_t rows_total, int64_t cols, uint8_t* q, uint8_t* s,
                               hipStream_t st) {
   if (rows_total == 0 || cols == 0) return hipSuccess;
-  dim3 grid((unsigned)((cols + 255) / 256), (unsigned)(rows_total / 32));
+  dim3 grid((unsigned)((cols + 511) / 512), (unsigned)(rows_total / 32));
   hipLaunchKernelGGL(quant_32x32_kernel, grid, dim3(256), 0, st, x, cols, q, s);
   return hipGetLastError();
 }
