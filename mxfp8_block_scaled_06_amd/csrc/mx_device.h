@@ -84,6 +84,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> packed bf16 pair, round to nearest even, with the
+// hardware convert (one v_cvt_pk_bf16_f32); finite results equal
+// pack_bf16x2's.
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
+  const bf16x2_t h = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 // Max across the 4 lanes of a DPP quad.
 __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));  // [1,0,3,2]

@@ -28,12 +28,16 @@
 //    read as zeros without clamping code.  Scales use the GEMM layout
 //    [K/128][rows][4] so one stage's scales for 256 rows are one 1 KiB line
 //    run per operand.
-//  * Operand fragments roll through registers: each 32-row fragment is
-//    refilled from LDS as soon as its last MFMA has issued, so LDS latency
-//    hides behind the remaining MFMAs.  One barrier per stage, placed after
-//    the first MFMAs of the stage's second half: past it, every wave has
-//    finished reading the other LDS buffer, which then receives the loads of
-//    the stage after next (a full stage of latency budget).
+//  * LDS bandwidth bounds this loop: a stage moves 64 KiB of DMA writes and
+//    128 KiB of fragment reads through the LDS, and measured on gfx950 the
+//    two serialize to about as long as the stage's 32 MFMAs per wave.  So
+//    MFMAs must never wait on a fragment read queued behind DMA writes: the
+//    fragments of the two MFMA windows of a stage live in two register sets,
+//    and while one window's 16 MFMAs run the other set is refilled for the
+//    next window.  One barrier per stage, at the start of its second window:
+//    every wave has then finished reading the stage's buffer, which receives
+//    the DMA of the stage after next (issued two loads per MFMA up front, for
+//    the longest latency budget), and the next stage has landed.
 //  * Tile scheduler on the device: the group offsets never cross to the host.
 //    Mode 0 enumerates (expert, M-tile) pairs from the offsets; tiles are
 //    ordered in bands of 8 N-tiles so concurrently running workgroups share
@@ -44,6 +48,8 @@
 //    neutral scale; empty wgrad groups store zeros.
 #include "mx_device.h"
 #include "mx_kernels.h"
+
+#include <type_traits>
 
 namespace mxk {
 
@@ -301,13 +307,17 @@ __device__ __forceinline__ v16f mfma(const Frag& y, const Frag& x, v16f c) {
 __device__ __forceinline__ void stage_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
-// Prologue: stage 0 landed while the first 12 loads of stage 1 may fly.
-__device__ __forceinline__ void first_barrier() {
-  asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-static_assert(kDmaPerStage == 17, "12 loads of a stage issue in one stage, 5 in the next");
+static_assert(kDmaPerStage == 17, "the prologue waits with vmcnt(17)");
 
 #define MX_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+template <int M, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (M < N) {
+    f(std::integral_constant<int, M>{});
+    static_for<M + 1, N>(f);
+  }
+}
 
 template <int MODE, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
@@ -366,29 +376,35 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) pc[w][c] = ((4 * w + half + 2 * c) ^ sw) << 4;
     const int yrow0 = jw * 128 + l32, xrow0 = iw * 128 + l32;
-    Frag X[4], Y[4];
+    // Operand sets of the two MFMA windows of a stage: [0..3] X sub-tiles,
+    // [4..7] Y sub-tiles.  While one window's 16 MFMAs run from one set, the
+    // other set is refilled from LDS for the next window, so every fragment
+    // read has a whole window of MFMAs to land.
+    Frag F0[8], F1[8];
+    // fragment `f` of window `w` of the stage in LDS buffer `st`
+    auto read = [&](const uint8_t* st, int w, int soffv, int nvalidv, int f, Frag& dst) {
+      if (f < 4) {
+        read_frag<MODE == 1>(st, st + 2 * kTileBytes, xrow0 + 32 * f, pc[w][0], pc[w][1], w, half, soffv, nvalidv, dst);
+      } else {
+        read_frag<MODE == 1>(st + kTileBytes, st + 2 * kTileBytes + 2 * kScaleChunk, yrow0 + 32 * (f - 4), pc[w][0],
+                             pc[w][1], w, half, soffv, nvalidv, dst);
+      }
+    };
+    // refill order: what the next window's first MFMAs need comes first
+    constexpr int kOrder[8] = {0, 4, 5, 6, 7, 1, 2, 3};
 
-    // DMA issue is spread one load per MFMA: loads 0..11 of stage s+2 follow
-    // the 12 MFMAs after stage s's barrier, loads 12..16 the first 5 MFMAs
-    // of stage s+1, all before stage s+1's barrier waits for them.
     {
       const StageDma d0 = make_stage_dma(smem, 0, L, k0, 0, ns, wv);
       issue_loads<0, 17>(d0, L, wv, lane);
+      const StageDma d1 = make_stage_dma(smem, 1, L, k0, 1, ns, wv);
+      issue_loads<0, 17>(d1, L, wv, lane);
     }
-    StageDma pend = make_stage_dma(smem, 1, L, k0, 1, ns, wv);
-    issue_loads<0, 12>(pend, L, wv, lane);
-    first_barrier();   // stage 0 has landed
+    asm volatile("s_waitcnt vmcnt(17) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stage 0 has landed
     {
-      const uint8_t* st = smem;
       const int soff = (int)((k0 >> 5) & 3);
       const int nvalid = (int)min((int64_t)4, (k1 - k0) >> 5);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        read_frag<MODE == 1>(st + kTileBytes, st + 2 * kTileBytes + 2 * kScaleChunk, yrow0 + q * 32, pc[0][0],
-                             pc[0][1], 0, half, soff, nvalid, Y[q]);
-        read_frag<MODE == 1>(st, st + 2 * kTileBytes, xrow0 + q * 32, pc[0][0], pc[0][1], 0, half, soff, nvalid,
-                             X[q]);
-      }
+      for (int f = 0; f < 8; ++f) read(smem, 0, soff, nvalid, f, F0[f]);
     }
     for (int kt = 0; kt < ns; ++kt) {
       const int buf = kt & 1;
@@ -401,104 +417,30 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
       const int soff_n = (int)((kn >> 5) & 3);
       const int nvalid_n = (int)min((int64_t)4, max((k1 - kn) >> 5, (int64_t)0));
 
-      // ---- window 0 of stage kt; refill with window 1 of stage kt; finish
-      // ---- the DMA of stage kt+1 (loads 12..16) ----
-      acc[0][0] = mfma(Y[0], X[0], acc[0][0]);
-      issue_load<12>(pend, L, wv, lane);
-      MX_FENCE();
-      acc[1][0] = mfma(Y[1], X[0], acc[1][0]);
-      issue_load<13>(pend, L, wv, lane);
-      MX_FENCE();
-      acc[2][0] = mfma(Y[2], X[0], acc[2][0]);
-      issue_load<14>(pend, L, wv, lane);
-      MX_FENCE();
-      acc[3][0] = mfma(Y[3], X[0], acc[3][0]);
-      issue_load<15>(pend, L, wv, lane);
-      MX_FENCE();
-      read_frag<MODE == 1>(cs, cs + 2 * kTileBytes, xrow0, pc[1][0], pc[1][1], 1, half, soff, nvalid, X[0]);
-      MX_FENCE();
-      acc[0][1] = mfma(Y[0], X[1], acc[0][1]);
-      issue_load<16>(pend, L, wv, lane);
-      MX_FENCE();
+      // ---- window 0 of stage kt from F0; F1 <- window 1 of stage kt ----
 #pragma unroll
-      for (int qy = 1; qy < 4; ++qy) acc[qy][1] = mfma(Y[qy], X[1], acc[qy][1]);
-      read_frag<MODE == 1>(cs, cs + 2 * kTileBytes, xrow0 + 32, pc[1][0], pc[1][1], 1, half, soff, nvalid, X[1]);
-      MX_FENCE();
-#pragma unroll
-      for (int qy = 0; qy < 4; ++qy) acc[qy][2] = mfma(Y[qy], X[2], acc[qy][2]);
-      read_frag<MODE == 1>(cs, cs + 2 * kTileBytes, xrow0 + 64, pc[1][0], pc[1][1], 1, half, soff, nvalid, X[2]);
-      MX_FENCE();
-#pragma unroll
-      for (int qy = 0; qy < 4; ++qy) {
-        acc[qy][3] = mfma(Y[qy], X[3], acc[qy][3]);
-        read_frag<MODE == 1>(cs + kTileBytes, cs + 2 * kTileBytes + 2 * kScaleChunk, yrow0 + qy * 32, pc[1][0],
-                             pc[1][1], 1, half, soff, nvalid, Y[qy]);
+      for (int m = 0; m < 16; ++m) {
+        const int qx = m >> 2, qy = m & 3;
+        acc[qy][qx] = mfma(F0[4 + qy], F0[qx], acc[qy][qx]);
+        if (m < 8) read(cs, 1, soff, nvalid, kOrder[m], F1[kOrder[m]]);
+        MX_FENCE();
       }
-      read_frag<MODE == 1>(cs, cs + 2 * kTileBytes, xrow0 + 96, pc[1][0], pc[1][1], 1, half, soff, nvalid, X[3]);
-      MX_FENCE();
-
-      // ---- window 1 of stage kt; refill with window 0 of stage kt+1; start
-      // ---- the DMA of stage kt+2 into this buffer (loads 0..11) ----
-#pragma unroll
-      for (int qy = 0; qy < 4; ++qy) acc[qy][0] = mfma(Y[qy], X[0], acc[qy][0]);
-      MX_FENCE();
+      // ---- window 1 of stage kt from F1; F0 <- window 0 of stage kt+1;
+      // ---- DMA of stage kt+2 into this stage's buffer ----
       stage_barrier();   // stage kt+1 landed; every wave is done reading buffer `buf`
-      pend = make_stage_dma(smem, buf, L, k0, kt + 2, ns, wv);
-      read_frag<MODE == 1>(nst, nst + 2 * kTileBytes, xrow0, pc[0][0], pc[0][1], 0, half, soff_n, nvalid_n, X[0]);
-      MX_FENCE();
-      acc[0][1] = mfma(Y[0], X[1], acc[0][1]);
-      issue_load<0>(pend, L, wv, lane);
-      MX_FENCE();
-      acc[1][1] = mfma(Y[1], X[1], acc[1][1]);
-      issue_load<1>(pend, L, wv, lane);
-      MX_FENCE();
-      acc[2][1] = mfma(Y[2], X[1], acc[2][1]);
-      issue_load<2>(pend, L, wv, lane);
-      MX_FENCE();
-      acc[3][1] = mfma(Y[3], X[1], acc[3][1]);
-      issue_load<3>(pend, L, wv, lane);
-      MX_FENCE();
-      read_frag<MODE == 1>(nst, nst + 2 * kTileBytes, xrow0 + 32, pc[0][0], pc[0][1], 0, half, soff_n, nvalid_n,
-                           X[1]);
-      MX_FENCE();
-      acc[0][2] = mfma(Y[0], X[2], acc[0][2]);
-      issue_load<4>(pend, L, wv, lane);
-      MX_FENCE();
-      acc[1][2] = mfma(Y[1], X[2], acc[1][2]);
-      issue_load<5>(pend, L, wv, lane);
-      MX_FENCE();
-      acc[2][2] = mfma(Y[2], X[2], acc[2][2]);
-      issue_load<6>(pend, L, wv, lane);
-      MX_FENCE();
-      acc[3][2] = mfma(Y[3], X[2], acc[3][2]);
-      issue_load<7>(pend, L, wv, lane);
-      MX_FENCE();
-      read_frag<MODE == 1>(nst, nst + 2 * kTileBytes, xrow0 + 64, pc[0][0], pc[0][1], 0, half, soff_n, nvalid_n,
-                           X[2]);
-      MX_FENCE();
-      acc[0][3] = mfma(Y[0], X[3], acc[0][3]);
-      issue_load<8>(pend, L, wv, lane);
-      MX_FENCE();
-      read_frag<MODE == 1>(nst + kTileBytes, nst + 2 * kTileBytes + 2 * kScaleChunk, yrow0, pc[0][0], pc[0][1], 0,
-                           half, soff_n, nvalid_n, Y[0]);
-      acc[1][3] = mfma(Y[1], X[3], acc[1][3]);
-      issue_load<9>(pend, L, wv, lane);
-      MX_FENCE();
-      read_frag<MODE == 1>(nst + kTileBytes, nst + 2 * kTileBytes + 2 * kScaleChunk, yrow0 + 32, pc[0][0],
-                           pc[0][1], 0, half, soff_n, nvalid_n, Y[1]);
-      acc[2][3] = mfma(Y[2], X[3], acc[2][3]);
-      issue_load<10>(pend, L, wv, lane);
-      MX_FENCE();
-      read_frag<MODE == 1>(nst + kTileBytes, nst + 2 * kTileBytes + 2 * kScaleChunk, yrow0 + 64, pc[0][0],
-                           pc[0][1], 0, half, soff_n, nvalid_n, Y[2]);
-      acc[3][3] = mfma(Y[3], X[3], acc[3][3]);
-      issue_load<11>(pend, L, wv, lane);
-      MX_FENCE();
-      read_frag<MODE == 1>(nst + kTileBytes, nst + 2 * kTileBytes + 2 * kScaleChunk, yrow0 + 96, pc[0][0],
-                           pc[0][1], 0, half, soff_n, nvalid_n, Y[3]);
-      read_frag<MODE == 1>(nst, nst + 2 * kTileBytes, xrow0 + 96, pc[0][0], pc[0][1], 0, half, soff_n, nvalid_n,
-                           X[3]);
-      MX_FENCE();
+      const StageDma pend = make_stage_dma(smem, buf, L, k0, kt + 2, ns, wv);
+      static_for<0, 16>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        constexpr int qx = m >> 2, qy = m & 3;
+        acc[qy][qx] = mfma(F1[4 + qy], F1[qx], acc[qy][qx]);
+        if constexpr (m < 8) {   // two loads per MFMA up front
+          issue_load<2 * m>(pend, L, wv, lane);
+          issue_load<2 * m + 1>(pend, L, wv, lane);
+        }
+        if constexpr (m == 8) issue_load<16>(pend, L, wv, lane);
+        if constexpr (m < 8) read(nst, 0, soff_n, nvalid_n, kOrder[m], F0[kOrder[m]]);
+        MX_FENCE();
+      });
     }
     // drain the empty-range loads still in flight before the workgroup ends
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -525,8 +467,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
           } else {
             uint16_t* crow = (uint16_t*)a.C + c_off + i * a.ldc;
             v2i w;
-            w[0] = (int)pack_bf16x2(v[4 * g + 0], v[4 * g + 1]);
-            w[1] = (int)pack_bf16x2(v[4 * g + 2], v[4 * g + 3]);
+            w[0] = (int)pack_bf16x2_rne(v[4 * g + 0], v[4 * g + 1]);
+            w[1] = (int)pack_bf16x2_rne(v[4 * g + 2], v[4 * g + 3]);
             *(v2i*)(crow + j) = w;
           }
         }
