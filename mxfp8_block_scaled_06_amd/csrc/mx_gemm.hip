@@ -63,9 +63,11 @@ constexpr int kScaleChunk = kBM * 4;              // one [rows][4] scale chunk: 
 constexpr int kStageBytes = 2 * kTileBytes + 4 * kScaleChunk;
 constexpr int kDmaPerStage = 8 + 8 + 1;           // per wave: X data, Y data, one scale chunk
 constexpr int kMaxExpertsLds = 1024;
+constexpr int kOutPitch = kBN * 2 + 16;          // bytes per staged bf16 output row (+16: spreads banks)
 constexpr int kRsrcWord3 = 0x00020000;            // raw buffer, 32-bit elements (gfx9 family)
 
 static_assert(kBM == kBN, "operand tiles share the load code");
+static_assert(kBM * kOutPitch <= 2 * kStageBytes, "the bf16 output tile fits the stage buffers");
 
 // 16-byte piece swizzle of a 128-byte LDS row: the 32 lanes that read one
 // logical piece of 32 consecutive rows spread over all bank groups.
@@ -450,32 +452,61 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
   // register group g, columns j0 + jw*128 + qy*32 + 8g + 4*half + 0..3.
   const int64_t c_off = MODE == 1 ? (int64_t)e * a.c_estride : 0;
   const int64_t i_lim = x_end;
+  if (OUT_F32) {
 #pragma unroll
-  for (int qx = 0; qx < 4; ++qx) {
-    const int64_t i = i0 + iw * 128 + qx * 32 + l32;
-    if (i >= i_lim) continue;
+    for (int qx = 0; qx < 4; ++qx) {
+      const int64_t i = i0 + iw * 128 + qx * 32 + l32;
+      if (i >= i_lim) continue;
 #pragma unroll
-    for (int qy = 0; qy < 4; ++qy) {
+      for (int qy = 0; qy < 4; ++qy) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t j = j0 + jw * 128 + qy * 32 + 8 * g + 4 * half;
-        if (j < a.J) {
-          const v16f& v = acc[qy][qx];
-          if (OUT_F32) {
+        for (int g = 0; g < 4; ++g) {
+          const int64_t j = j0 + jw * 128 + qy * 32 + 8 * g + 4 * half;
+          if (j < a.J) {
+            const v16f& v = acc[qy][qx];
             float* crow = (float*)a.C + c_off + i * a.ldc;
             *(float4*)(crow + j) = make_float4(v[4 * g + 0], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
-          } else {
-            uint16_t* crow = (uint16_t*)a.C + c_off + i * a.ldc;
-            v2i w;
-            w[0] = (int)pack_bf16x2_rne(v[4 * g + 0], v[4 * g + 1]);
-            w[1] = (int)pack_bf16x2_rne(v[4 * g + 2], v[4 * g + 3]);
-            *(v2i*)(crow + j) = w;
           }
         }
+        // one 32x32 tile at a time: keeps the accumulator reads from being
+        // hoisted all at once (register pressure)
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // one 32x32 tile at a time: keeps the accumulator reads from being
-      // hoisted all at once (register pressure)
-      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    // bf16: the tile goes through the (now idle) LDS stage buffers so every
+    // store instruction writes two whole 512-byte row segments instead of
+    // 16-byte pieces of 32 rows.
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // nobody reads the stages now
+    uint8_t* ot = smem;   // [256 rows][kOutPitch bytes]
+#pragma unroll
+    for (int qx = 0; qx < 4; ++qx) {
+      const int row = iw * 128 + qx * 32 + l32;
+#pragma unroll
+      for (int qy = 0; qy < 4; ++qy) {
+        const v16f& v = acc[qy][qx];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = jw * 128 + qy * 32 + 8 * g + 4 * half;
+          v2i w;
+          w[0] = (int)pack_bf16x2_rne(v[4 * g + 0], v[4 * g + 1]);
+          w[1] = (int)pack_bf16x2_rne(v[4 * g + 2], v[4 * g + 3]);
+          *(v2i*)(ot + row * kOutPitch + col * 2) = w;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+    // thread t: 16 bytes (8 columns) of row 8*it + t/32; the J % 8 == 0
+    // contract makes an 8-column group wholly valid or wholly past J
+    const int c8 = (tid & 31) * 8;
+    const int64_t j = j0 + c8;
+#pragma unroll 4
+    for (int it = 0; it < kBM / 8; ++it) {
+      const int row = it * 8 + (tid >> 5);
+      const int64_t i = i0 + row;
+      const v4i w = *(const v4i*)(ot + row * kOutPitch + c8 * 2);
+      if (i < i_lim && j < a.J) *(v4i*)((uint16_t*)a.C + c_off + i * a.ldc + j) = w;
     }
   }
 }
