@@ -91,7 +91,8 @@ struct TileDesc {
   int e;
   int64_t i0, i_end;   // rows of X (output rows) covered: [i0, min(i0 + kBM, i_end))
   int64_t j0;
-  int64_t k0, k1;      // contraction range [k0, k1)
+  int64_t k0, k1;      // contraction stages cover [k0, k1), k0 a multiple of kBK
+  int64_t k_lo;        // blocks before k_lo are masked (a wgrad group start)
 };
 
 // Wave-0 scan of per-expert M-tile counts (mode 0).  pref[e] = number of
@@ -166,6 +167,7 @@ __device__ __forceinline__ TileDesc decode_tile(const GemmArgs& a, int* s_offs, 
     d.j0 = nt * kBN;
     d.k0 = 0;
     d.k1 = a.Kc;
+    d.k_lo = 0;
     d.valid = 1;
   } else {
     const int64_t nti = (a.I + kBM - 1) / kBM;
@@ -191,8 +193,10 @@ __device__ __forceinline__ TileDesc decode_tile(const GemmArgs& a, int* s_offs, 
     d.i0 = it * kBM;
     d.i_end = a.I;
     d.j0 = jt * kBN;
-    d.k0 = st;
+    // whole lines and one scale chunk per stage; an empty group has no stages
+    d.k0 = en > st ? (st & ~(int64_t)(kBK - 1)) : st;
     d.k1 = en;
+    d.k_lo = st;
     d.valid = 1;
   }
   return d;
@@ -278,25 +282,36 @@ struct Frag {
 // Read the operand of one 32-row sub-tile (this lane's `row`) for MFMA window
 // `w` (0/1) of a stage: pieces 4w + half and 4w + half + 2 of the row, and
 // the scale byte of block 2w + half.  `soff` = byte offset of the stage's
-// first block inside the staged scale chunks (0..3).  With MASKED, blocks at
-// or past `nvalid` are zeroed and their scale lanes made neutral.
+// first block inside the staged scale chunks (0..3).  With MASKED, only the
+// stage's blocks [vr & 255, vr >> 8) keep their data; the others are zeroed
+// and their scale lanes made neutral.
 template <bool MASKED>
 __device__ __forceinline__ void read_frag(const uint8_t* tile, const uint8_t* sc, int row, int pa, int pb,
-                                          int w, int half, int soff, int nvalid, Frag& f) {
+                                          int w, int half, int soff, int vr, Frag& f) {
   const v4i a0 = *(const v4i*)(tile + row * kBK + pa);
   const v4i a1 = *(const v4i*)(tile + row * kBK + pb);
   const int t = soff + 2 * w + half;
   int scale = sc[(t >> 2) * kScaleChunk + row * 4 + (t & 3)];
   v4i b0 = a0, b1 = a1;
   if (MASKED) {
-    const int keep0 = (2 * w) < nvalid ? -1 : 0;       // chunk 0 of every lane lies in block 2w
-    const int keep1 = (2 * w + 1) < nvalid ? -1 : 0;   // chunk 1 in block 2w + 1
+    const int vlo = vr & 255, vhi = vr >> 8;
+    const int b0i = 2 * w, b1i = 2 * w + 1, bh = 2 * w + half;   // chunk 0, chunk 1, this lane's scale
+    const int keep0 = (b0i >= vlo && b0i < vhi) ? -1 : 0;
+    const int keep1 = (b1i >= vlo && b1i < vhi) ? -1 : 0;
     b0 &= (v4i){keep0, keep0, keep0, keep0};
     b1 &= (v4i){keep1, keep1, keep1, keep1};
-    scale = (2 * w + half) < nvalid ? scale : 127;
+    scale = (bh >= vlo && bh < vhi) ? scale : 127;
   }
   f.v = (v8i){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
   f.s = scale;
+}
+
+// Valid-block range of the stage starting at contraction byte kk, packed as
+// lo | hi << 8 (stage-relative blocks 0..4).
+__device__ __forceinline__ int stage_valid(int64_t kk, int64_t k_lo, int64_t k1) {
+  const int64_t lo = k_lo > kk ? (k_lo - kk) >> 5 : 0;
+  const int64_t hi = k1 > kk ? (k1 - kk) >> 5 : 0;
+  return (int)min(lo, (int64_t)4) | ((int)min(hi, (int64_t)4) << 8);
 }
 
 __device__ __forceinline__ v16f mfma(const Frag& y, const Frag& x, v16f c) {
@@ -339,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
   // tile description, made wave-uniform (it is identical for every thread)
   const int e = uni32(td0.e);
   const int64_t i0 = uni64(td0.i0), i_end = uni64(td0.i_end), j0 = uni64(td0.j0);
-  const int64_t k0 = uni64(td0.k0), k1 = uni64(td0.k1);
+  const int64_t k0 = uni64(td0.k0), k1 = uni64(td0.k1), k_lo = uni64(td0.k_lo);
   const int64_t x_end = MODE == 0 ? i_end : a.I;
   const int64_t rows_x = min((int64_t)kBM, x_end - i0);
   const int64_t rows_y = min((int64_t)kBN, a.J - j0);
@@ -404,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
     asm volatile("s_waitcnt vmcnt(17) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stage 0 has landed
     {
       const int soff = (int)((k0 >> 5) & 3);
-      const int nvalid = (int)min((int64_t)4, (k1 - k0) >> 5);
+      const int nvalid = stage_valid(k0, k_lo, k1);
 #pragma unroll
       for (int f = 0; f < 8; ++f) read(smem, 0, soff, nvalid, f, F0[f]);
     }
@@ -414,10 +429,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
       const uint8_t* nst = smem + (buf ^ 1) * kStageBytes;    // next stage
       const int64_t kk = k0 + (int64_t)kt * kBK;
       const int soff = (int)((kk >> 5) & 3);
-      const int nvalid = (int)min((int64_t)4, (k1 - kk) >> 5);
+      const int nvalid = stage_valid(kk, k_lo, k1);
       const int64_t kn = kk + kBK;
       const int soff_n = (int)((kn >> 5) & 3);
-      const int nvalid_n = (int)min((int64_t)4, max((k1 - kn) >> 5, (int64_t)0));
+      const int nvalid_n = stage_valid(kn, k_lo, k1);
 
       // ---- window 0 of stage kt from F0; F1 <- window 1 of stage kt ----
 #pragma unroll
