@@ -4,11 +4,16 @@ One step = one training pass of the routed-expert grouped GEMMs over one
 batch of routed tokens, Llama4-Scout-shaped (E=16 experts, 16384 tokens
 routed top-1 by a uniform multinomial, K=5120, N=8192, groups padded with
 zero rows to multiples of 32):
-    forward  out = A @ W[e]^T      (quantize A and W rowwise, grouped GEMM)
-    dgrad    dA  = dOut @ W[e]     (quantize dOut rowwise, W colwise, GEMM)
+    weights  W -> both MX orientations in one pass (mx_quantize_weights; the
+             weights change once per optimizer step)
+    forward  out = A @ W[e]^T      (quantize A rowwise, grouped GEMM)
+    dgrad    dA  = dOut @ W[e]     (quantize dOut rowwise, GEMM on W's
+                                    colwise orientation)
     wgrad    dW  = dOut^T @ A      (quantize dOut and A along tokens, GEMM)
-each through the library's bf16 entry points, so every quantize kernel, the
-tile scheduler, the GEMM main loop and the bf16 epilogue run in the step.
+through the library's entry points, so every quantize kernel, the tile
+scheduler, the GEMM main loop and the bf16 epilogue run in the step.  The
+same step through the three all-bf16 entry points (weights quantized twice)
+is timed too and reported as `step_bf16_entry_points_ms`.
 
 Printed: one JSON line.  `value` = algorithmic GEMM TFLOP/s of the whole
 step (2*M*N*K per GEMM on the real tokens, quantization time included).
@@ -154,25 +159,32 @@ def main():
     dA = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     dW = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
     ws = {op: torch.empty(mx.mx_grouped_mm_workspace_bytes(op, M, N, K, E), dtype=torch.uint8, device=dev)
-          for op in (mx.OP_FWD, mx.OP_DGRAD, mx.OP_WGRAD)}
+          for op in (mx.OP_FWD_Q, mx.OP_DGRAD_Q, mx.OP_WGRAD)}
+    wq = (torch.empty((E, N, K), dtype=torch.uint8, device=dev),
+          torch.empty((E, K // 128, N, 4), dtype=torch.uint8, device=dev),
+          torch.empty((E, K, N), dtype=torch.uint8, device=dev),
+          torch.empty((E, N // 128, K, 4), dtype=torch.uint8, device=dev))
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        mx.mx_grouped_mm_fwd(A, W, offs, out=out, ws=ws[mx.OP_FWD])
+        qW, sW, qWt, sWt = mx.mx_quantize_weights(W, *wq)
         if ev is not None:
             ev[1].record()
-        mx.mx_grouped_mm_dgrad(G, W, offs, out=dA, ws=ws[mx.OP_DGRAD])
+        mx.mx_grouped_mm_fwd_q(A, qW, sW, offs, out=out, ws=ws[mx.OP_FWD_Q])
         if ev is not None:
             ev[2].record()
-        mx.mx_grouped_mm_wgrad(G, A, offs, out=dW, ws=ws[mx.OP_WGRAD])
+        mx.mx_grouped_mm_dgrad_q(G, qWt, sWt, offs, out=dA, ws=ws[mx.OP_DGRAD_Q])
         if ev is not None:
             ev[3].record()
+        mx.mx_grouped_mm_wgrad(G, A, offs, out=dW, ws=ws[mx.OP_WGRAD])
+        if ev is not None:
+            ev[4].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -186,19 +198,33 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
     prim_ms = {name: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
-               for i, name in enumerate(("fwd", "dgrad", "wgrad"))}
+               for i, name in enumerate(("weights", "fwd", "dgrad", "wgrad"))}
     gemm_flops_real = 3 * 2.0 * m_real * N * K
     gemm_flops_pad = 3 * 2.0 * M * N * K
     value = gemm_flops_real / (ms_per_step * 1e-3) / 1e12
     log(f"step {ms_per_step:.3f} ms ({prim_ms}); wall {wall:.2f}s for {args.steps} steps")
 
+    # the same step through the three all-bf16 entry points (W quantized twice)
+    ws_bf = {op: torch.empty(mx.mx_grouped_mm_workspace_bytes(op, M, N, K, E), dtype=torch.uint8, device=dev)
+             for op in (mx.OP_FWD, mx.OP_DGRAD)}
+
+    def step_bf16():
+        mx.mx_grouped_mm_fwd(A, W, offs, out=out, ws=ws_bf[mx.OP_FWD])
+        mx.mx_grouped_mm_dgrad(G, W, offs, out=dA, ws=ws_bf[mx.OP_DGRAD])
+        mx.mx_grouped_mm_wgrad(G, A, offs, out=dW, ws=ws[mx.OP_WGRAD])
+
+    step_bf16()
+    torch.cuda.synchronize()
+    tb = time_launches(torch, step_bf16, max(2, args.steps // 2))
+    log(f"step through the bf16 entry points: {tb['mean_ms']:.3f} ms")
+    del ws_bf
+
     # ---------------- GEMM only, prequantized operands ----------------
     g = mx.mx_scales_to_gemm_layout
     qA, sA = mx.mx_quantize_rowwise(A)
-    qW, sW = mx.mx_quantize_rowwise(W)
     qG, sG = mx.mx_quantize_rowwise(G)
-    qWt, sWt = mx.mx_quantize_colwise(W)
-    sA, sW, sG, sWt = g(sA), g(sW), g(sG), g(sWt)
+    sA, sG = g(sA), g(sG)
+    qW, sW, qWt, sWt = wq
     # wgrad operands: the token axis is the contraction axis, padded to a
     # multiple of 128 with zero rows (the layout the bf16 entry point uses)
     Mp = (M + 127) // 128 * 128
@@ -250,6 +276,8 @@ def main():
         s_col = torch.empty((C, R // 32), dtype=torch.uint8, device=dev)
         s_sq = torch.empty((R // 32, C // 32), dtype=torch.uint8, device=dev)
         for name, fn, nbytes in (
+                ("weights_both_orientations", lambda: mx.mx_quantize_weights(W, *wq),
+                 E * N * K * 4 + 2 * E * N * K // 32),
                 ("rowwise", lambda: mx.mx_quantize_rowwise(X, q, s_row), 3 * R * C + R * C // 32),
                 ("colwise", lambda: mx.mx_quantize_colwise(X, qt, s_col), 3 * R * C + R * C // 32),
                 ("32x32", lambda: mx.mx_quantize_32x32(X, q, s_sq), 3 * R * C + R * C // 1024)):
@@ -259,7 +287,7 @@ def main():
             gbs = nbytes / (t["mean_ms"] * 1e-3) / 1e9
             quant[name] = {"ms": t["mean_ms"], "GB_s": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS,
                            "bytes": nbytes}
-            log(f"quant {name} [{R},{C}]: {t['mean_ms']:.3f} ms  {gbs:.0f} GB/s  {100 * gbs / PEAK_HBM_GBS:.1f}%")
+            log(f"quant {name}: {t['mean_ms']:.3f} ms  {gbs:.0f} GB/s  {100 * gbs / PEAK_HBM_GBS:.1f}%")
         del X, q, s_row, qt, s_col, s_sq
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -296,9 +324,10 @@ def main():
                    "E": E, "tokens": m_real, "rows_padded": M, "K": K, "N": N},
         "frac_of_peak": value / PEAK_MXFP8_TFLOPS,
         "step_breakdown_ms": prim_ms,
+        "step_bf16_entry_points_ms": tb["mean_ms"],
         "step_tflops_on_padded_rows": gemm_flops_pad / (ms_per_step * 1e-3) / 1e12,
         "gemm_only": gemm,
-        "quant_sweep_65600x5120": quant,
+        "quant_sweep_65600x5120": quant,   # plus the [16, 8192, 5120] weights in both orientations
         "roofline": roofline,
         "cpu_baseline": cpu,
         "gpu": torch.cuda.get_device_name(0),

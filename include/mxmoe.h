@@ -162,14 +162,14 @@ mx_status mx_grouped_gemm_mx_f32(const uint8_t* X, const uint8_t* sX, const uint
 /* Bytes of workspace the bf16 entry point `op` needs (0 on invalid sizes). */
 size_t mx_grouped_mm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int64_t E);
 
-/* out [M, N] = A [M, K] @ W[e] [N, K]^T per group.  Requires K % 32 == 0,
+/* out [M, N] = A [M, K] @ W[e] [N, K]^T per group.  Requires K % 128 == 0,
  * N % 8 == 0. */
 mx_status mx_grouped_mm_fwd(const uint16_t* A, const uint16_t* W, const int32_t* offs,
                             int64_t M, int64_t N, int64_t K, int64_t E, uint16_t* out,
                             void* ws, size_t ws_bytes, void* stream);
 
 /* dA [M, K] = dOut [M, N] @ W[e] [N, K] per group; W is quantized in 32-blocks
- * along N.  Requires N % 32 == 0, K % 8 == 0. */
+ * along N.  Requires N % 128 == 0, K % 8 == 0. */
 mx_status mx_grouped_mm_dgrad(const uint16_t* dOut, const uint16_t* W, const int32_t* offs,
                               int64_t M, int64_t N, int64_t K, int64_t E, uint16_t* dA,
                               void* ws, size_t ws_bytes, void* stream);
@@ -180,6 +180,40 @@ mx_status mx_grouped_mm_dgrad(const uint16_t* dOut, const uint16_t* W, const int
 mx_status mx_grouped_mm_wgrad(const uint16_t* dOut, const uint16_t* A, const int32_t* offs,
                               int64_t M, int64_t N, int64_t K, int64_t E, uint16_t* dW,
                               void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Prequantized expert weights: the weight 4-tuple of the MoK expert PR
+ * review (weight_fp8 / weight_scale feed the forward, weight_t_fp8 /
+ * weight_t_scale the backward).  Weights change once per optimizer step, so
+ * both orientations are quantized once, in one pass that reads W once, and
+ * reused by the forward and the dgrad of that step.
+ * ------------------------------------------------------------------------ */
+
+/* W [E, N, K] -> q [E, N, K] (1x32 blocks along K) with s in the GEMM scale
+ * layout [E, K/128, N, 4], and q_t [E, K, N] (32x1 blocks along N, stored
+ * transposed) with s_t in the GEMM scale layout [E, N/128, K, 4].  Requires
+ * N % 128 == 0 and K % 128 == 0.  Bit-identical to mx_quantize_rowwise and
+ * mx_quantize_colwise followed by mx_scales_to_gemm_layout.  w, q, q_t
+ * 16-byte aligned; s, s_t 4-byte aligned. */
+mx_status mx_quantize_weights(const uint16_t* w, int64_t E, int64_t N, int64_t K, uint8_t* q, uint8_t* s,
+                              uint8_t* q_t, uint8_t* s_t, void* stream);
+
+/* Workspaces of the two entry points below (they quantize only the
+ * activation side). */
+#define MX_OP_FWD_Q 3
+#define MX_OP_DGRAD_Q 4
+
+/* mx_grouped_mm_fwd with W given as (q, s) of mx_quantize_weights: the
+ * result is bit-identical.  Requires K % 128 == 0, N % 8 == 0. */
+mx_status mx_grouped_mm_fwd_q(const uint16_t* A, const uint8_t* qW, const uint8_t* sW, const int32_t* offs,
+                              int64_t M, int64_t N, int64_t K, int64_t E, uint16_t* out,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* mx_grouped_mm_dgrad with W given as (q_t, s_t) of mx_quantize_weights: the
+ * result is bit-identical.  Requires N % 128 == 0, K % 8 == 0. */
+mx_status mx_grouped_mm_dgrad_q(const uint16_t* dOut, const uint8_t* qWt, const uint8_t* sWt,
+                                const int32_t* offs, int64_t M, int64_t N, int64_t K, int64_t E,
+                                uint16_t* dA, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

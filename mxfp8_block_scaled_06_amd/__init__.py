@@ -22,7 +22,7 @@ __all__ = [
     "OP_FWD", "OP_DGRAD", "OP_WGRAD",
 ]
 
-OP_FWD, OP_DGRAD, OP_WGRAD = 0, 1, 2
+OP_FWD, OP_DGRAD, OP_WGRAD, OP_FWD_Q, OP_DGRAD_Q = 0, 1, 2, 3, 4
 _STATUS = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN", 4: "MX_ERR_WORKSPACE",
            5: "MX_ERR_HIP"}
 
@@ -70,6 +70,12 @@ def load_library():
         f = getattr(lib, name)
         f.restype = c_int
         f.argtypes = [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]
+    lib.mx_quantize_weights.restype = c_int
+    lib.mx_quantize_weights.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]
+    for name in ("mx_grouped_mm_fwd_q", "mx_grouped_mm_dgrad_q"):
+        f = getattr(lib, name)
+        f.restype = c_int
+        f.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]
     _lib = lib
     return lib
 
@@ -284,4 +290,73 @@ def mx_grouped_mm_wgrad(dOut, A, offs, out=None, ws=None):
     _check("mx_grouped_mm_wgrad",
            lib.mx_grouped_mm_wgrad(_ptr(dOut), _ptr(A), _ptr(offs), M, N, K, E, _ptr(out), _ptr(ws), ws.numel(),
                                    _stream(A.device)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Prequantized expert weights (both orientations in one pass)
+# ---------------------------------------------------------------------------
+def mx_quantize_weights(W, q=None, s=None, q_t=None, s_t=None):
+    """W bf16 [E, N, K] -> (q [E, N, K], s [E, K/128, N, 4], q_t [E, K, N], s_t [E, N/128, K, 4]):
+    rowwise codes along K and colwise codes along N (stored transposed), scales
+    in the GEMM layout.  N and K must be multiples of 128."""
+    import torch
+    lib = load_library()
+    _require(W, torch.bfloat16, "W")
+    if W.dim() != 3:
+        raise ValueError("W must be [E, N, K]")
+    E, N, K = W.shape
+    dev = W.device
+    if q is None:
+        q = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+    if s is None:
+        s = torch.empty((E, K // 128, N, 4), dtype=torch.uint8, device=dev)
+    if q_t is None:
+        q_t = torch.empty((E, K, N), dtype=torch.uint8, device=dev)
+    if s_t is None:
+        s_t = torch.empty((E, N // 128, K, 4), dtype=torch.uint8, device=dev)
+    _check("mx_quantize_weights", lib.mx_quantize_weights(_ptr(W), E, N, K, _ptr(q), _ptr(s), _ptr(q_t), _ptr(s_t),
+                                                          _stream(dev)))
+    return q, s, q_t, s_t
+
+
+def mx_grouped_mm_fwd_q(A, qW, sW, offs, out=None, ws=None):
+    """mx_grouped_mm_fwd with W given as (q, s) of mx_quantize_weights."""
+    import torch
+    lib = load_library()
+    _require(A, torch.bfloat16, "A")
+    _require(qW, torch.uint8, "qW")
+    _require(sW, torch.uint8, "sW")
+    _require(offs, torch.int32, "offs")
+    M, K = A.shape
+    E, N, K2 = qW.shape
+    if K2 != K:
+        raise ValueError(f"A has K={K} but qW has K={K2}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    ws = _ws(OP_FWD_Q, M, N, K, E, A.device, ws)
+    _check("mx_grouped_mm_fwd_q",
+           lib.mx_grouped_mm_fwd_q(_ptr(A), _ptr(qW), _ptr(sW), _ptr(offs), M, N, K, E, _ptr(out), _ptr(ws),
+                                   ws.numel(), _stream(A.device)))
+    return out
+
+
+def mx_grouped_mm_dgrad_q(dOut, qWt, sWt, offs, out=None, ws=None):
+    """mx_grouped_mm_dgrad with W given as (q_t, s_t) of mx_quantize_weights."""
+    import torch
+    lib = load_library()
+    _require(dOut, torch.bfloat16, "dOut")
+    _require(qWt, torch.uint8, "qWt")
+    _require(sWt, torch.uint8, "sWt")
+    _require(offs, torch.int32, "offs")
+    M, N = dOut.shape
+    E, K, N2 = qWt.shape
+    if N2 != N:
+        raise ValueError(f"dOut has N={N} but qWt has N={N2}")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=dOut.device)
+    ws = _ws(OP_DGRAD_Q, M, N, K, E, dOut.device, ws)
+    _check("mx_grouped_mm_dgrad_q",
+           lib.mx_grouped_mm_dgrad_q(_ptr(dOut), _ptr(qWt), _ptr(sWt), _ptr(offs), M, N, K, E, _ptr(out), _ptr(ws),
+                                     ws.numel(), _stream(dOut.device)))
     return out

@@ -70,6 +70,14 @@ WsLayout ws_layout(int op, int64_t M, int64_t N, int64_t K, int64_t E) {
     sz[1] = (size_t)M * (K / 32);
     sz[2] = (size_t)E * N * K;
     sz[3] = (size_t)E * N * (K / 32);
+  } else if (op == MX_OP_FWD_Q) {
+    sz[0] = (size_t)M * K;
+    sz[1] = (size_t)M * (K / 32);
+    sz[2] = sz[3] = 0;
+  } else if (op == MX_OP_DGRAD_Q) {
+    sz[0] = (size_t)M * N;
+    sz[1] = (size_t)M * (N / 32);
+    sz[2] = sz[3] = 0;
   } else if (op == MX_OP_DGRAD) {
     sz[0] = (size_t)M * N;
     sz[1] = (size_t)M * (N / 32);
@@ -213,7 +221,7 @@ mx_status mx_scales_to_gemm_layout(const uint8_t* s, int64_t batch, int64_t rows
 }
 
 size_t mx_grouped_mm_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int64_t E) {
-  if (op < MX_OP_FWD || op > MX_OP_WGRAD || M < 0 || N < 0 || K < 0 || E < 1) return 0;
+  if (op < MX_OP_FWD || op > MX_OP_DGRAD_Q || M < 0 || N < 0 || K < 0 || E < 1) return 0;
   return ws_layout(op, M, N, K, E).total;
 }
 
@@ -288,6 +296,64 @@ mx_status mx_grouped_mm_wgrad(const uint16_t* dOut, const uint16_t* A, const int
       MX_OK)
     return st;
   return mx_grouped_gemm_mx(qGt, sGt, qAt, sAt, offs, 1, N, K, Mp, E, dW, stream);
+}
+
+mx_status mx_quantize_weights(const uint16_t* w, int64_t E, int64_t N, int64_t K, uint8_t* q, uint8_t* s,
+                              uint8_t* q_t, uint8_t* s_t, void* stream) {
+  const char* fn = "mx_quantize_weights";
+  if (E < 1 || N < 0 || K < 0)
+    return fail(MX_ERR_SHAPE, "%s: E=%lld N=%lld K=%lld", fn, (long long)E, (long long)N, (long long)K);
+  if (N % 128 != 0 || K % 128 != 0)
+    return fail(MX_ERR_SHAPE, "%s: N=%lld and K=%lld must be multiples of 128", fn, (long long)N, (long long)K);
+  if (N == 0 || K == 0) return MX_OK;
+  if (N / 128 > 65535 || K / 128 > 65535 || E > 65535) return fail(MX_ERR_SHAPE, "%s: too large for one launch", fn);
+  if (!w || !q || !s || !q_t || !s_t) return fail(MX_ERR_NULL, "%s: null pointer", fn);
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(q_t, 16) || !aligned(s, 4) || !aligned(s_t, 4))
+    return fail(MX_ERR_ALIGN, "%s: w, q, q_t must be 16-byte and s, s_t 4-byte aligned", fn);
+  return hip_status(mxk::launch_quant_dual(w, E, N, K, q, s, q_t, s_t, (hipStream_t)stream), fn);
+}
+
+mx_status mx_grouped_mm_fwd_q(const uint16_t* A, const uint8_t* qW, const uint8_t* sW, const int32_t* offs, int64_t M,
+                              int64_t N, int64_t K, int64_t E, uint16_t* out, void* ws, size_t ws_bytes,
+                              void* stream) {
+  const char* fn = "mx_grouped_mm_fwd_q";
+  mx_status st = check_mm(fn, A, qW, offs, out, M, N, K, E);
+  if (st != MX_OK) return st;
+  if (!sW) return fail(MX_ERR_NULL, "%s: null weight scales", fn);
+  if (K % 128 != 0) return fail(MX_ERR_SHAPE, "%s: K=%lld is not a multiple of 128", fn, (long long)K);
+  if (N % 8 != 0) return fail(MX_ERR_SHAPE, "%s: N=%lld is not a multiple of 8", fn, (long long)N);
+  const WsLayout L = ws_layout(MX_OP_FWD_Q, M, N, K, E);
+  if (!ws || ws_bytes < L.total)
+    return fail(MX_ERR_WORKSPACE, "%s: workspace of %zu bytes at %p, need %zu", fn, ws_bytes, ws, L.total);
+  if (!aligned(ws, 256)) return fail(MX_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  if (M == 0 || N == 0) return MX_OK;
+  uint8_t* w8 = (uint8_t*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *qA = w8 + L.off[0], *sA = w8 + L.off[1];
+  if ((st = hip_status(mxk::launch_quant_rowwise(A, M, K, qA, sA, M, s), "fwd_q quantize A")) != MX_OK) return st;
+  return mx_grouped_gemm_mx(qA, sA, qW, sW, offs, 0, M, N, K, E, out, stream);
+}
+
+mx_status mx_grouped_mm_dgrad_q(const uint16_t* dOut, const uint8_t* qWt, const uint8_t* sWt, const int32_t* offs,
+                                int64_t M, int64_t N, int64_t K, int64_t E, uint16_t* dA, void* ws, size_t ws_bytes,
+                                void* stream) {
+  const char* fn = "mx_grouped_mm_dgrad_q";
+  mx_status st = check_mm(fn, dOut, qWt, offs, dA, M, N, K, E);
+  if (st != MX_OK) return st;
+  if (!sWt) return fail(MX_ERR_NULL, "%s: null weight scales", fn);
+  if (N % 128 != 0) return fail(MX_ERR_SHAPE, "%s: N=%lld is not a multiple of 128", fn, (long long)N);
+  if (K % 8 != 0) return fail(MX_ERR_SHAPE, "%s: K=%lld is not a multiple of 8", fn, (long long)K);
+  const WsLayout L = ws_layout(MX_OP_DGRAD_Q, M, N, K, E);
+  if (!ws || ws_bytes < L.total)
+    return fail(MX_ERR_WORKSPACE, "%s: workspace of %zu bytes at %p, need %zu", fn, ws_bytes, ws, L.total);
+  if (!aligned(ws, 256)) return fail(MX_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  if (M == 0 || K == 0) return MX_OK;
+  uint8_t* w8 = (uint8_t*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *qG = w8 + L.off[0], *sG = w8 + L.off[1];
+  if ((st = hip_status(mxk::launch_quant_rowwise(dOut, M, N, qG, sG, M, s), "dgrad_q quantize dOut")) != MX_OK)
+    return st;
+  return mx_grouped_gemm_mx(qG, sG, qWt, sWt, offs, 0, M, K, N, E, dA, stream);
 }
 
 }  // extern "C"

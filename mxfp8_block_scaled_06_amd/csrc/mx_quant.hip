@@ -183,6 +183,120 @@ __global__ __launch_bounds__(256) void quant_colwise_kernel(const uint16_t* __re
 }
 
 // ---------------------------------------------------------------------------
+// Both orientations of expert weights in one pass: w [E, N, K] ->
+//   q   [E, N, K] (1x32 blocks along K), s   GEMM layout [E][K/128][N][4]
+//   q_t [E, K, N] (32x1 blocks along N), s_t GEMM layout [E][N/128][K][4]
+// (N % 128 == 0, K % 128 == 0).  A workgroup stages a 128 (n) x 128 (k) bf16
+// tile in LDS once; the rowwise half quantizes its rows straight to q (four
+// threads fill one 128-byte line), the colwise half is the colwise kernel's
+// path (column pairs, codes transposed back through LDS for whole-line
+// stores).  HBM traffic 4 + 1/16 bytes per element instead of two passes of
+// 3 + 1/32.  Operation: the weight 4-tuple of the MoK expert PR review
+// (weight_fp8 / weight_scale for the forward, weight_t_fp8 / weight_t_scale
+// for the backward).
+// ---------------------------------------------------------------------------
+constexpr int kDualPitch = 272;   // bytes per staged input row (256 + 16): conflict-free row and column reads
+
+__global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restrict__ w, int64_t N, int64_t K,
+                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ s,
+                                                         uint8_t* __restrict__ q_t, uint8_t* __restrict__ s_t) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kColTile * kDualPitch];
+  const int tid = threadIdx.x;
+  const int64_t b = blockIdx.z;
+  const int64_t n0 = (int64_t)blockIdx.y * kColTile;
+  const int64_t k0 = (int64_t)blockIdx.x * kColTile;
+  const uint16_t* wb = w + b * N * K;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int chunk = it * 256 + tid;
+    const int rr = chunk >> 4, cc = chunk & 15;
+    const v4i v = __builtin_nontemporal_load((const v4i*)(wb + (n0 + rr) * K + k0 + cc * 8));
+    *(v4i*)(tile + rr * kDualPitch + cc * 16) = v;
+  }
+  __syncthreads();
+
+  // ---- rowwise: task = (row, block of 32 along k); threads 4r..4r+3 share a row
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int task = h * 256 + tid;
+    const int row = task >> 2, blk = task & 3;
+    v4i x[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x[c] = *(const v4i*)(tile + row * kDualPitch + blk * 64 + c * 16);
+    uint32_t am = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) am = max(am, absmax8(x[c]));
+    const uint32_t byte = e8m0_from_absbits(am);
+    const float m = inv_scale_from_e8m0(byte == 0xFFu ? 127u : byte);
+    v4i o0, o1;
+    {
+      const v2i c0 = byte == 0xFFu ? (v2i){0x7F7F7F7F, 0x7F7F7F7F} : quant8(x[0], m);
+      const v2i c1 = byte == 0xFFu ? (v2i){0x7F7F7F7F, 0x7F7F7F7F} : quant8(x[1], m);
+      const v2i c2 = byte == 0xFFu ? (v2i){0x7F7F7F7F, 0x7F7F7F7F} : quant8(x[2], m);
+      const v2i c3 = byte == 0xFFu ? (v2i){0x7F7F7F7F, 0x7F7F7F7F} : quant8(x[3], m);
+      o0 = (v4i){c0[0], c0[1], c1[0], c1[1]};
+      o1 = (v4i){c2[0], c2[1], c3[0], c3[1]};
+    }
+    uint8_t* qp = q + (b * N + n0 + row) * K + k0 + blk * 32;
+    *(v4i*)qp = o0;
+    *(v4i*)(qp + 16) = o1;
+    // [E][K/128][N][4]: the tile's 128 columns are one chunk
+    s[b * (K / 32) * N + (k0 >> 7) * N * 4 + (n0 + row) * 4 + blk] = (uint8_t)byte;
+  }
+
+  // ---- colwise: wave w quantizes rows [32w, 32w+32) of columns 2l, 2l+1
+  const int wv = tid >> 6, lane = tid & 63;
+  uint32_t v[32];
+  uint32_t am0 = 0, am1 = 0;
+#pragma unroll
+  for (int t = 0; t < 32; ++t) {
+    v[t] = *(const uint32_t*)(tile + (32 * wv + t) * kDualPitch + 4 * lane);
+    am0 = max(am0, v[t] & 0x7FFFu);
+    am1 = max(am1, (v[t] >> 16) & 0x7FFFu);
+  }
+  const uint32_t byte0 = e8m0_from_absbits(am0), byte1 = e8m0_from_absbits(am1);
+  const float m0 = inv_scale_from_e8m0(byte0 == 0xFFu ? 127u : byte0);
+  const float m1 = inv_scale_from_e8m0(byte1 == 0xFFu ? 127u : byte1);
+  v4i out0[2], out1[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int t = hh * 16 + d * 4;
+      int a = cvt2_e4m3<false>(bf16lo(v[t]) * m0, bf16lo(v[t + 1]) * m0, 0);
+      a = cvt2_e4m3<true>(bf16lo(v[t + 2]) * m0, bf16lo(v[t + 3]) * m0, a);
+      int c = cvt2_e4m3<false>(bf16hi(v[t]) * m1, bf16hi(v[t + 1]) * m1, 0);
+      c = cvt2_e4m3<true>(bf16hi(v[t + 2]) * m1, bf16hi(v[t + 3]) * m1, c);
+      out0[hh][d] = byte0 == 0xFFu ? 0x7F7F7F7F : a;
+      out1[hh][d] = byte1 == 0xFFu ? 0x7F7F7F7F : c;
+    }
+  }
+  __syncthreads();   // both halves are done reading the input: the tile becomes the output stage
+  uint8_t* o8 = tile;
+  uint8_t* sc = o8 + kColTile * kColPitch;   // [128 output rows][4 blocks]
+  *(v4i*)(o8 + (2 * lane) * kColPitch + 32 * wv) = out0[0];
+  *(v4i*)(o8 + (2 * lane) * kColPitch + 32 * wv + 16) = out0[1];
+  *(v4i*)(o8 + (2 * lane + 1) * kColPitch + 32 * wv) = out1[0];
+  *(v4i*)(o8 + (2 * lane + 1) * kColPitch + 32 * wv + 16) = out1[1];
+  sc[(2 * lane) * 4 + wv] = (uint8_t)byte0;
+  sc[(2 * lane + 1) * 4 + wv] = (uint8_t)byte1;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int p = j * 256 + tid;
+    const int orow = p >> 3, pc = p & 7;
+    const v4i x = *(const v4i*)(o8 + orow * kColPitch + 16 * pc);
+    *(v4i*)(q_t + (b * K + k0 + orow) * N + n0 + 16 * pc) = x;
+  }
+  if (tid < kColTile) {
+    // [E][N/128][K][4]: blocks n0/32 .. n0/32 + 3 of output row k0 + tid
+    *(uint32_t*)(s_t + b * (N / 32) * K + (n0 >> 7) * K * 4 + (k0 + tid) * 4) = *(const uint32_t*)(sc + tid * 4);
+  }
+}
+
+static_assert(kColTile * kColPitch + kColTile * 4 <= kColTile * kDualPitch, "output stage fits the input tile");
+
+// ---------------------------------------------------------------------------
 // 32x32: x viewed as [rows, cols] (batch folded into rows; rows % 32 == 0).
 // A workgroup covers 32 rows x 512 columns; wave w covers columns
 // [128w, 128w+128) = four 32x32 tiles.  Lane l holds 8 columns (chunk l%16) of
@@ -232,6 +346,14 @@ hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows_total, int64_t c
   const int64_t grid = (nchunks + per_block - 1) / per_block;
   hipLaunchKernelGGL(quant_rowwise_kernel, dim3((unsigned)grid), dim3(kRowThreads), 0, st, x, nchunks, q, s,
                      (uint32_t)(cols / 32), (uint32_t)gemm_rows_per_batch);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_dual(const uint16_t* w, int64_t E, int64_t N, int64_t K, uint8_t* q, uint8_t* s,
+                             uint8_t* q_t, uint8_t* s_t, hipStream_t st) {
+  if (E == 0 || N == 0 || K == 0) return hipSuccess;
+  dim3 grid((unsigned)(K / kColTile), (unsigned)(N / kColTile), (unsigned)E);
+  hipLaunchKernelGGL(quant_dual_kernel, grid, dim3(256), 0, st, w, N, K, q, s, q_t, s_t);
   return hipGetLastError();
 }
 

@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("mx_quantize_rowwise", "mx_quantize_colwise", "mx_quantize_32x32", "mx_grouped_mm_fwd",
               "mx_grouped_mm_dgrad", "mx_grouped_mm_wgrad", "mx_grouped_gemm_mx",
-              "mx_grouped_mm_workspace_bytes", "mx_last_error", "mx_version"):
+              "mx_grouped_mm_workspace_bytes", "mx_last_error", "mx_version", "mx_quantize_weights",
+              "mx_grouped_mm_fwd_q", "mx_grouped_mm_dgrad_q"):
         assert n in names
 
 
@@ -84,6 +85,27 @@ def test_gemm_validation_errors():
     assert lib.mx_grouped_mm_wgrad(FAKE, FAKE, FAKE, 250, 64, 64, 2, FAKE, FAKE, 1 << 40, None) == 2
     assert lib.mx_grouped_mm_dgrad(FAKE, FAKE, FAKE, 256, 96, 64, 2, FAKE, FAKE, 1 << 40, None) == 2
     assert lib.mx_grouped_mm_workspace_bytes(7, 1, 1, 1, 1) == 0
+
+
+def test_prequantized_weight_entry_points_validate():
+    lib = _lib()
+    q = lib.mx_quantize_weights
+    assert q(FAKE, 2, 256, 200, FAKE, FAKE, FAKE, FAKE, None) == 2       # K % 128
+    assert "multiples of 128" in _err(lib)
+    assert q(FAKE, 2, 96, 256, FAKE, FAKE, FAKE, FAKE, None) == 2        # N % 128
+    assert q(FAKE, 0, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == 2       # E < 1
+    assert q(FAKE, 1, 128, 128, FAKE, FAKE, None, FAKE, None) == 1       # null q_t
+    assert q(FAKE, 1, 128, 128, FAKE, FAKE + 2, FAKE, FAKE, None) == 3   # misaligned s
+    assert q(None, 1, 0, 128, None, None, None, None, None) == 0         # empty: nothing to do
+    f = lib.mx_grouped_mm_fwd_q
+    need = lib.mx_grouped_mm_workspace_bytes(3, 256, 512, 256, 2)
+    assert 256 * 256 * 33 // 32 <= need < lib.mx_grouped_mm_workspace_bytes(0, 256, 512, 256, 2)
+    assert f(FAKE, FAKE, FAKE, FAKE, 256, 512, 256, 2, FAKE, FAKE, need - 1, None) == 4   # workspace
+    assert f(FAKE, FAKE, None, FAKE, 256, 512, 256, 2, FAKE, FAKE, need, None) == 1       # null scales
+    assert f(FAKE, FAKE, FAKE, FAKE, 256, 512, 224, 2, FAKE, FAKE, 1 << 40, None) == 2    # K % 128
+    d = lib.mx_grouped_mm_dgrad_q
+    assert d(FAKE, FAKE, FAKE, FAKE, 256, 96, 64, 2, FAKE, FAKE, 1 << 40, None) == 2      # N % 128
+    assert lib.mx_grouped_mm_workspace_bytes(4, 256, 512, 256, 2) >= 256 * 512 * 33 // 32
 
 
 def test_workspace_sizes_cover_both_operands():
