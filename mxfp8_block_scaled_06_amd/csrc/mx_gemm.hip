@@ -513,7 +513,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
     }
     __syncthreads();
     // thread t: 16 bytes (8 columns) of row 8*it + t/32; the J % 8 == 0
-    // contract makes an 8-column group wholly valid or wholly past J
+    // contract makes an 8-column group wholly valid or wholly past J.
+    // Streaming (nontemporal) stores: the output is not read back here and
+    // should not evict the operand rows the other workgroups share in L2.
     const int c8 = (tid & 31) * 8;
     const int64_t j = j0 + c8;
 #pragma unroll 4
@@ -521,7 +523,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
       const int row = it * 8 + (tid >> 5);
       const int64_t i = i0 + row;
       const v4i w = *(const v4i*)(ot + row * kOutPitch + c8 * 2);
-      if (i < i_lim && j < a.J) *(v4i*)((uint16_t*)a.C + c_off + i * a.ldc + j) = w;
+      if (i < i_lim && j < a.J) __builtin_nontemporal_store(w, (v4i*)((uint16_t*)a.C + c_off + i * a.ldc + j));
     }
   }
 }
