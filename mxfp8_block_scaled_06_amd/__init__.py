@@ -360,3 +360,9 @@ def mx_grouped_mm_dgrad_q(dOut, qWt, sWt, offs, out=None, ws=None):
            lib.mx_grouped_mm_dgrad_q(_ptr(dOut), _ptr(qWt), _ptr(sWt), _ptr(offs), M, N, K, E, _ptr(out), _ptr(ws),
                                      ws.numel(), _stream(dOut.device)))
     return out
+
+
+def mx_grouped_mm(A, W, offs):
+    """Differentiable MXFP8 grouped GEMM (forward, dgrad, wgrad in the library's kernels)."""
+    from .autograd import mx_grouped_mm as _f
+    return _f(A, W, offs)

@@ -123,3 +123,18 @@ def test_binding_refuses_cpu_tensors():
     _lib()
     with pytest.raises(ValueError, match="GPU tensor"):
         mx.mx_quantize_rowwise(torch.zeros((4, 64), dtype=torch.bfloat16))
+
+
+def test_differentiable_primitive_rejects_bad_contracts():
+    """Clear errors before any kernel: the shapes the composed kernels need."""
+    import torch
+    bf = torch.bfloat16
+    offs = torch.tensor([64], dtype=torch.int32)
+    with pytest.raises(ValueError, match="multiples of 128"):
+        mx.mx_grouped_mm(torch.zeros((64, 96), dtype=bf), torch.zeros((1, 128, 96), dtype=bf), offs)
+    with pytest.raises(ValueError, match="multiple of 32"):
+        mx.mx_grouped_mm(torch.zeros((48, 128), dtype=bf), torch.zeros((1, 128, 128), dtype=bf), offs)
+    with pytest.raises(TypeError, match="bfloat16"):
+        mx.mx_grouped_mm(torch.zeros((64, 128)), torch.zeros((1, 128, 128), dtype=bf), offs)
+    with pytest.raises(ValueError, match="one entry per expert"):
+        mx.mx_grouped_mm(torch.zeros((64, 128), dtype=bf), torch.zeros((2, 128, 128), dtype=bf), offs)
