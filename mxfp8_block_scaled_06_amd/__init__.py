@@ -366,3 +366,9 @@ def mx_grouped_mm(A, W, offs):
     """Differentiable MXFP8 grouped GEMM (forward, dgrad, wgrad in the library's kernels)."""
     from .autograd import mx_grouped_mm as _f
     return _f(A, W, offs)
+
+
+def mx_linear(x, weight):
+    """Differentiable dense MXFP8 linear y = x @ weight^T (one expert of mx_grouped_mm)."""
+    from .autograd import mx_linear as _f
+    return _f(x, weight)

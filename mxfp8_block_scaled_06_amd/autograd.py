@@ -84,3 +84,17 @@ def mx_grouped_mm(A, W, offs):
     """Differentiable out[g_e] = A[g_e] @ W[e]^T with MXFP8 operands (see the module docstring)."""
     _check(A, W, offs)
     return _MXGroupedMM.get().apply(A.contiguous(), W.contiguous(), offs)
+
+
+def mx_linear(x, weight):
+    """Differentiable dense MXFP8 linear y = x @ weight^T (x bf16 [M, K], weight bf16 [N, K]):
+    the one-expert case of mx_grouped_mm (the dense half of "MoE + dense" in the
+    pytorch/ao PR benchmarks).  Same contract with E = 1: M % 32 == 0,
+    N % 128 == 0, K % 128 == 0."""
+    import torch
+    if weight.dim() != 2:
+        raise ValueError("mx_linear: weight must be [N, K]")
+    if x.dim() != 2:
+        raise ValueError("mx_linear: x must be [M, K]")
+    offs = torch.tensor([x.shape[0]], dtype=torch.int32, device=x.device)
+    return mx_grouped_mm(x, weight.unsqueeze(0), offs)

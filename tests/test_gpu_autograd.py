@@ -100,3 +100,29 @@ def test_autograd_only_requested_gradients():
     out = mx.mx_grouped_mm(A, W, offs)
     out.sum().backward()
     assert A.grad is not None and W.grad is None
+
+
+def test_dense_linear_is_one_expert():
+    """mx_linear: E = 1 of the grouped primitive; gradients within the GEMM
+    criterion of the oracle (dense matmuls of the dequantized operands)."""
+    torch = require_gpu()
+    import mxfp8_block_scaled_06_amd as mx
+    M, N, K = 160, 256, 384
+    A = inp.random_bf16((M, K), seed=1400, outliers=True)
+    W = inp.random_bf16((N, K), seed=1401, std=0.02)
+    G = inp.random_bf16((M, N), seed=1402, std=1e-3)
+    log(f"dense linear M={M} N={N} K={K}")
+    x = to_dev_bf16(A).requires_grad_(True)
+    w = to_dev_bf16(W).requires_grad_(True)
+    y = mx.mx_linear(x, w)
+    y.backward(to_dev_bf16(G))
+    offs = np.array([M], dtype=np.int32)
+    for name, got, ref, absr in (
+            ("y", y, oracle.grouped_mm_fwd(A, W[None], offs), oracle.grouped_mm_fwd(A, W[None], offs, absolute=True)),
+            ("dx", x.grad, oracle.grouped_mm_dgrad(G, W[None], offs),
+             oracle.grouped_mm_dgrad(G, W[None], offs, absolute=True)),
+            ("dw", w.grad, oracle.grouped_mm_wgrad(G, A, offs)[0],
+             oracle.grouped_mm_wgrad(G, A, offs, absolute=True)[0])):
+        rep = oracle.r1_check(bf16_host_bits(got.detach()), ref, abs_terms=absr)
+        assert rep["ok"], (name, rep)
+    assert w.grad.shape == (N, K)
