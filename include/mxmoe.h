@@ -182,6 +182,19 @@ mx_status mx_grouped_mm_wgrad(const uint16_t* dOut, const uint16_t* A, const int
                               void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Token gather fused into the rowwise quantizer (the rowwise-A quantization
+ * done inside the token gather of the MoE dispatch).  Output row r holds the
+ * codes of x[rows[r], :]; an index < 0 or >= src_rows gives a zero row (the
+ * padding of expert groups to 32 rows).  x [src_rows, cols] bf16, rows int32
+ * [M] on the device, q [M, cols], s_gemm in the GEMM scale layout
+ * [cols/128, M, 4]: (q, s_gemm) is X of mx_grouped_gemm_mx as it stands.
+ * Requires cols % 128 == 0.  Bit-identical to gathering the rows and calling
+ * mx_quantize_rowwise then mx_scales_to_gemm_layout.
+ * ------------------------------------------------------------------------ */
+mx_status mx_quantize_rowwise_gather(const uint16_t* x, int64_t src_rows, const int32_t* rows, int64_t M,
+                                     int64_t cols, uint8_t* q, uint8_t* s_gemm, void* stream);
+
+/* ------------------------------------------------------------------------
  * Prequantized expert weights: the weight 4-tuple of the MoK expert PR
  * review (weight_fp8 / weight_scale feed the forward, weight_t_fp8 /
  * weight_t_scale the backward).  Weights change once per optimizer step, so

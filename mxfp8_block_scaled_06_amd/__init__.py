@@ -70,6 +70,8 @@ def load_library():
         f = getattr(lib, name)
         f.restype = c_int
         f.argtypes = [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]
+    lib.mx_quantize_rowwise_gather.restype = c_int
+    lib.mx_quantize_rowwise_gather.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp]
     lib.mx_quantize_weights.restype = c_int
     lib.mx_quantize_weights.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]
     for name in ("mx_grouped_mm_fwd_q", "mx_grouped_mm_dgrad_q"):
@@ -372,3 +374,21 @@ def mx_linear(x, weight):
     """Differentiable dense MXFP8 linear y = x @ weight^T (one expert of mx_grouped_mm)."""
     from .autograd import mx_linear as _f
     return _f(x, weight)
+
+
+def mx_quantize_rowwise_gather(x, rows, q=None, s=None):
+    """Rowwise MX quantization of x[rows[r]] (rows int32 [M]; a negative index gives a zero row).
+    Returns (q uint8 [M, cols], s uint8 [cols/128, M, 4] in the GEMM scale layout)."""
+    import torch
+    lib = load_library()
+    _require(x, torch.bfloat16, "x")
+    _require(rows, torch.int32, "rows")
+    src_rows, cols = x.shape
+    M = rows.shape[0]
+    if q is None:
+        q = torch.empty((M, cols), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((cols // 128, M, 4), dtype=torch.uint8, device=x.device)
+    _check("mx_quantize_rowwise_gather",
+           lib.mx_quantize_rowwise_gather(_ptr(x), src_rows, _ptr(rows), M, cols, _ptr(q), _ptr(s), _stream(x.device)))
+    return q, s

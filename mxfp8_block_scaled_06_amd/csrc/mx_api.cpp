@@ -356,4 +356,20 @@ mx_status mx_grouped_mm_dgrad_q(const uint16_t* dOut, const uint8_t* qWt, const 
   return mx_grouped_gemm_mx(qG, sG, qWt, sWt, offs, 0, M, K, N, E, dA, stream);
 }
 
+mx_status mx_quantize_rowwise_gather(const uint16_t* x, int64_t src_rows, const int32_t* rows, int64_t M,
+                                     int64_t cols, uint8_t* q, uint8_t* s_gemm, void* stream) {
+  const char* fn = "mx_quantize_rowwise_gather";
+  if (src_rows < 0 || M < 0 || cols < 0)
+    return fail(MX_ERR_SHAPE, "%s: src_rows=%lld M=%lld cols=%lld", fn, (long long)src_rows, (long long)M,
+                (long long)cols);
+  if (cols % 128 != 0) return fail(MX_ERR_SHAPE, "%s: cols=%lld is not a multiple of 128", fn, (long long)cols);
+  if (M == 0 || cols == 0) return MX_OK;
+  if (M * (cols / 8) >= ((int64_t)1 << 40) || M >= ((int64_t)1 << 31))
+    return fail(MX_ERR_SHAPE, "%s: too large", fn);
+  if (!rows || !q || !s_gemm || (src_rows > 0 && !x)) return fail(MX_ERR_NULL, "%s: null pointer", fn);
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(rows, 4))
+    return fail(MX_ERR_ALIGN, "%s: x and q must be 16-byte aligned, rows 4-byte aligned", fn);
+  return hip_status(mxk::launch_quant_rowwise_gather(x, src_rows, rows, M, cols, q, s_gemm, (hipStream_t)stream), fn);
+}
+
 }  // extern "C"

@@ -30,6 +30,10 @@ struct GemmArgs {
 // GEMM scale layout [rows_total/R][cols/128][R][4] with R = gemm_rows_per_batch.
 hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows_total, int64_t cols, uint8_t* q, uint8_t* s,
                                 int64_t gemm_rows_per_batch, hipStream_t st);
+// Rowwise of x[rows[r]] for r < M (index < 0 or >= src_rows: a zero row);
+// scales in the GEMM layout [cols/128][M][4].
+hipError_t launch_quant_rowwise_gather(const uint16_t* x, int64_t src_rows, const int32_t* rows, int64_t M,
+                                       int64_t cols, uint8_t* q, uint8_t* s, hipStream_t st);
 // gemm_layout == 0: s_t [batch][cols][lds]; 1: GEMM layout [batch][ldq/128][cols][4].
 hipError_t launch_quant_colwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q_t,
                                 int64_t ldq, uint8_t* s_t, int64_t lds, int gemm_layout, hipStream_t st);

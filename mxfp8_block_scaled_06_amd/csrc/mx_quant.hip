@@ -79,6 +79,52 @@ __global__ __launch_bounds__(kRowThreads) void quant_rowwise_kernel(const uint16
 }
 
 // ---------------------------------------------------------------------------
+// Rowwise with the token gather fused in: output row r quantizes source row
+// rows[r] of x (a negative or out-of-range index gives a zero row, e.g. the
+// padding that rounds an expert group up to 32 rows).  Scales go straight to
+// the GEMM layout [cols/128][M][4], so the result feeds the grouped GEMM as X
+// with no gathered bf16 copy in between.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kRowThreads) void quant_rowwise_gather_kernel(const uint16_t* __restrict__ x,
+                                                                           int64_t src_rows,
+                                                                           const int32_t* __restrict__ rows,
+                                                                           int64_t nchunks, int64_t cols,
+                                                                           uint8_t* __restrict__ q,
+                                                                           uint8_t* __restrict__ s,
+                                                                           uint32_t chunks_per_row,
+                                                                           uint32_t out_rows) {
+  const int64_t base = (int64_t)blockIdx.x * (kRowThreads * kRowU) + threadIdx.x;
+  v4i w[kRowU];
+#pragma unroll
+  for (int u = 0; u < kRowU; ++u) {
+    const int64_t idx = base + (int64_t)u * kRowThreads;
+    w[u] = (v4i){0, 0, 0, 0};
+    if (idx < nchunks) {
+      const uint32_t r = (uint32_t)(idx / chunks_per_row);
+      const uint32_t c = (uint32_t)(idx - (int64_t)r * chunks_per_row);
+      const int64_t sr = rows[r];
+      if (sr >= 0 && sr < src_rows) w[u] = __builtin_nontemporal_load((const v4i*)(x + sr * cols + c * 8));
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kRowU; ++u) {
+    const int64_t idx = base + (int64_t)u * kRowThreads;
+    const uint32_t am = quad_max(absmax8(w[u]));   // quads never straddle rows (cols % 32 == 0)
+    if (idx < nchunks) {
+      const uint32_t byte = e8m0_from_absbits(am);
+      v2i codes;
+      if (byte == 0xFFu) {
+        codes = (v2i){0x7F7F7F7F, 0x7F7F7F7F};
+      } else {
+        codes = quant8(w[u], inv_scale_from_e8m0(byte));
+      }
+      *(v2i*)(q + idx * 8) = codes;
+      if ((threadIdx.x & 3) == 0) s[row_scale_index((uint32_t)(idx >> 2), chunks_per_row / 4, out_rows)] = (uint8_t)byte;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Colwise: x [batch, rows, cols] -> q_t [batch, cols, ldq], s_t (ldq >= rows).
 // A workgroup stages a 128x128 bf16 tile in LDS (coalesced 256-byte row
 // segments); wave w quantizes rows [32w, 32w+32) of the tile: lane l owns
@@ -354,6 +400,17 @@ hipError_t launch_quant_dual(const uint16_t* w, int64_t E, int64_t N, int64_t K,
   if (E == 0 || N == 0 || K == 0) return hipSuccess;
   dim3 grid((unsigned)(K / kColTile), (unsigned)(N / kColTile), (unsigned)E);
   hipLaunchKernelGGL(quant_dual_kernel, grid, dim3(256), 0, st, w, N, K, q, s, q_t, s_t);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rowwise_gather(const uint16_t* x, int64_t src_rows, const int32_t* rows, int64_t M,
+                                       int64_t cols, uint8_t* q, uint8_t* s, hipStream_t st) {
+  const int64_t nchunks = M * (cols / 8);
+  if (nchunks == 0) return hipSuccess;
+  const int64_t per_block = (int64_t)kRowThreads * kRowU;
+  const int64_t grid = (nchunks + per_block - 1) / per_block;
+  hipLaunchKernelGGL(quant_rowwise_gather_kernel, dim3((unsigned)grid), dim3(kRowThreads), 0, st, x, src_rows, rows,
+                     nchunks, cols, q, s, (uint32_t)(cols / 8), (uint32_t)M);
   return hipGetLastError();
 }
 

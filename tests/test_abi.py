@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     for n in ("mx_quantize_rowwise", "mx_quantize_colwise", "mx_quantize_32x32", "mx_grouped_mm_fwd",
               "mx_grouped_mm_dgrad", "mx_grouped_mm_wgrad", "mx_grouped_gemm_mx",
               "mx_grouped_mm_workspace_bytes", "mx_last_error", "mx_version", "mx_quantize_weights",
-              "mx_grouped_mm_fwd_q", "mx_grouped_mm_dgrad_q"):
+              "mx_grouped_mm_fwd_q", "mx_grouped_mm_dgrad_q", "mx_quantize_rowwise_gather"):
         assert n in names
 
 
@@ -106,6 +106,15 @@ def test_prequantized_weight_entry_points_validate():
     d = lib.mx_grouped_mm_dgrad_q
     assert d(FAKE, FAKE, FAKE, FAKE, 256, 96, 64, 2, FAKE, FAKE, 1 << 40, None) == 2      # N % 128
     assert lib.mx_grouped_mm_workspace_bytes(4, 256, 512, 256, 2) >= 256 * 512 * 33 // 32
+
+
+def test_gather_quantize_validates():
+    lib = _lib()
+    g = lib.mx_quantize_rowwise_gather
+    assert g(FAKE, 10, FAKE, 64, 96, FAKE, FAKE, None) == 2          # cols % 128
+    assert g(FAKE, 10, None, 64, 128, FAKE, FAKE, None) == 1         # null rows
+    assert g(FAKE + 8, 10, FAKE, 64, 128, FAKE, FAKE, None) == 3     # misaligned x
+    assert g(None, 0, None, 0, 128, None, None, None) == 0            # nothing to do
 
 
 def test_workspace_sizes_cover_both_operands():
