@@ -163,6 +163,11 @@ mx_status grouped_gemm_impl(const char* fn, const uint8_t* X, const uint8_t* sX,
     return fail(MX_ERR_SHAPE, "%s: number of experts E=%lld outside [1, %d]", fn, (long long)E, mxk::kMaxExperts);
   if (Kc % 128 != 0) return fail(MX_ERR_SHAPE, "%s: Kc=%lld is not a multiple of 128", fn, (long long)Kc);
   if (J % 8 != 0) return fail(MX_ERR_SHAPE, "%s: J=%lld is not a multiple of 8", fn, (long long)J);
+  // per-lane offsets inside a 256-row tile are 32-bit (row * Kc), and row
+  // indices of X and Y must fit an int
+  if (Kc > ((int64_t)1 << 23) || I >= ((int64_t)1 << 31) || J >= ((int64_t)1 << 31))
+    return fail(MX_ERR_SHAPE, "%s: too large (I=%lld J=%lld Kc=%lld; Kc <= 2^23)", fn, (long long)I, (long long)J,
+                (long long)Kc);
   const bool empty_out = (mode == 0) ? (I == 0 || J == 0) : (I == 0 || J == 0);
   if (empty_out) return MX_OK;
   if (!C || !offs) return fail(MX_ERR_NULL, "%s: null output or offsets", fn);

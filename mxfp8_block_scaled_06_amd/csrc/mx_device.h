@@ -73,23 +73,11 @@ __device__ __forceinline__ uint32_t absmax8(v4i w) {
   return m;
 }
 
-// fp32 -> bf16 bit pattern, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x40u) & 0xFFFFu;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
-}
-
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-// Two fp32 values -> packed bf16 pair, round to nearest even, with the
-// hardware convert (one v_cvt_pk_bf16_f32); finite results equal
-// pack_bf16x2's.
+// Two fp32 values -> packed bf16 pair (low half = lo), round to nearest
+// even, with the hardware convert (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
   const bf16x2_t h = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
   return __builtin_bit_cast(uint32_t, h);

@@ -76,6 +76,7 @@ def test_gemm_validation_errors():
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 64, 128, 5000, FAKE, None) == 2    # E too large
     assert f(FAKE, FAKE, None, FAKE, FAKE, 0, 64, 64, 128, 1, FAKE, None) == 1       # null Y
     assert f(FAKE, FAKE, FAKE + 4, FAKE, FAKE, 0, 64, 64, 128, 1, FAKE, None) == 3   # misaligned Y
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 64, (1 << 23) + 128, 1, FAKE, None) == 2   # Kc too large
     g = lib.mx_grouped_mm_fwd
     need = lib.mx_grouped_mm_workspace_bytes(0, 256, 512, 256, 2)
     assert need >= 256 * 256 + 2 * 512 * 256
