@@ -282,28 +282,43 @@ struct Frag {
 // Read the operand of one 32-row sub-tile (this lane's `row`) for MFMA window
 // `w` (0/1) of a stage: pieces 4w + half and 4w + half + 2 of the row, and
 // the scale byte of block 2w + half.  `soff` = byte offset of the stage's
-// first block inside the staged scale chunks (0..3).  With MASKED, only the
-// stage's blocks [vr & 255, vr >> 8) keep their data; the others are zeroed
-// and their scale lanes made neutral.
-template <bool MASKED>
-__device__ __forceinline__ void read_frag(const uint8_t* tile, const uint8_t* sc, int row, int pa, int pb,
-                                          int w, int half, int soff, int vr, Frag& f) {
+// first block inside the staged scale chunks (0..3).
+__device__ __forceinline__ void read_frag(const uint8_t* tile, const uint8_t* sc, int row, int pa, int pb, int w,
+                                          int half, int soff, Frag& f) {
   const v4i a0 = *(const v4i*)(tile + row * kBK + pa);
   const v4i a1 = *(const v4i*)(tile + row * kBK + pb);
   const int t = soff + 2 * w + half;
-  int scale = sc[(t >> 2) * kScaleChunk + row * 4 + (t & 3)];
-  v4i b0 = a0, b1 = a1;
-  if (MASKED) {
-    const int vlo = vr & 255, vhi = vr >> 8;
-    const int b0i = 2 * w, b1i = 2 * w + 1, bh = 2 * w + half;   // chunk 0, chunk 1, this lane's scale
-    const int keep0 = (b0i >= vlo && b0i < vhi) ? -1 : 0;
-    const int keep1 = (b1i >= vlo && b1i < vhi) ? -1 : 0;
-    b0 &= (v4i){keep0, keep0, keep0, keep0};
-    b1 &= (v4i){keep1, keep1, keep1, keep1};
-    scale = (bh >= vlo && bh < vhi) ? scale : 127;
-  }
-  f.v = (v8i){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-  f.s = scale;
+  f.s = sc[(t >> 2) * kScaleChunk + row * 4 + (t & 3)];
+  f.v = (v8i){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+}
+
+// Contraction-block mask of one MFMA window (wgrad: blocks of a stage that
+// lie outside the expert's group).  keep0/keep1 cover the window's two
+// blocks (the fragment's first and second 16-byte piece); `sel` is the byte
+// permute that keeps the lane's scale or substitutes the neutral 127.
+struct WinMask {
+  int keep0, keep1;
+  unsigned sel;
+};
+
+// Valid stage-relative blocks are [vr & 255, vr >> 8).
+__device__ __forceinline__ WinMask make_mask(int vr, int w, int half) {
+  const int vlo = vr & 255, vhi = vr >> 8;
+  const int b0 = 2 * w, b1 = 2 * w + 1, bh = 2 * w + half;
+  WinMask m;
+  m.keep0 = (b0 >= vlo && b0 < vhi) ? -1 : 0;
+  m.keep1 = (b1 >= vlo && b1 < vhi) ? -1 : 0;
+  m.sel = 0x0c0c0c00u | ((bh >= vlo && bh < vhi) ? 0u : 4u);
+  return m;
+}
+
+// Zero a fragment's masked blocks and neutralise its scale.  The scale goes
+// through a byte permute: written as a select, the compiler turns it into a
+// divergent branch around the scale load, which splits the main loop into
+// blocks and lets MFMAs sink past the stage barrier.
+__device__ __forceinline__ void mask_frag(Frag& f, const WinMask& m) {
+  f.v &= (v8i){m.keep0, m.keep0, m.keep0, m.keep0, m.keep1, m.keep1, m.keep1, m.keep1};
+  f.s = (int)__builtin_amdgcn_perm(127u, (unsigned)f.s, m.sel);
 }
 
 // Valid-block range of the stage starting at contraction byte kk, packed as
@@ -399,12 +414,22 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
     // read has a whole window of MFMAs to land.
     Frag F0[8], F1[8];
     // fragment `f` of window `w` of the stage in LDS buffer `st`
-    auto read = [&](const uint8_t* st, int w, int soffv, int nvalidv, int f, Frag& dst) {
+    auto read = [&](const uint8_t* st, int w, int soffv, int f, Frag& dst) {
       if (f < 4) {
-        read_frag<MODE == 1>(st, st + 2 * kTileBytes, xrow0 + 32 * f, pc[w][0], pc[w][1], w, half, soffv, nvalidv, dst);
+        read_frag(st, st + 2 * kTileBytes, xrow0 + 32 * f, pc[w][0], pc[w][1], w, half, soffv, dst);
       } else {
-        read_frag<MODE == 1>(st + kTileBytes, st + 2 * kTileBytes + 2 * kScaleChunk, yrow0 + 32 * (f - 4), pc[w][0],
-                             pc[w][1], w, half, soffv, nvalidv, dst);
+        read_frag(st + kTileBytes, st + 2 * kTileBytes + 2 * kScaleChunk, yrow0 + 32 * (f - 4), pc[w][0], pc[w][1], w,
+                  half, soffv, dst);
+      }
+    };
+    // wgrad masking is applied where a fragment is first used, not where it
+    // is read: an LDS wait right after each read would stall the MFMAs the
+    // read is meant to overlap
+    auto first_use = [&](Frag* F, int m, const WinMask& mk) {
+      if (MODE == 1) {
+        const int qx = m >> 2, qy = m & 3;
+        if (qx == 0) mask_frag(F[4 + qy], mk);
+        if (qy == 0) mask_frag(F[qx], mk);
       }
     };
     // refill order: what the next window's first MFMAs need comes first
@@ -419,9 +444,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
     asm volatile("s_waitcnt vmcnt(17) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stage 0 has landed
     {
       const int soff = (int)((k0 >> 5) & 3);
-      const int nvalid = stage_valid(k0, k_lo, k1);
 #pragma unroll
-      for (int f = 0; f < 8; ++f) read(smem, 0, soff, nvalid, f, F0[f]);
+      for (int f = 0; f < 8; ++f) read(smem, 0, soff, f, F0[f]);
     }
     for (int kt = 0; kt < ns; ++kt) {
       const int buf = kt & 1;
@@ -429,17 +453,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
       const uint8_t* nst = smem + (buf ^ 1) * kStageBytes;    // next stage
       const int64_t kk = k0 + (int64_t)kt * kBK;
       const int soff = (int)((kk >> 5) & 3);
-      const int nvalid = stage_valid(kk, k_lo, k1);
       const int64_t kn = kk + kBK;
       const int soff_n = (int)((kn >> 5) & 3);
-      const int nvalid_n = stage_valid(kn, k_lo, k1);
+      const int nvalid = MODE == 1 ? stage_valid(kk, k_lo, k1) : 0;
+      const WinMask mk0 = make_mask(nvalid, 0, half), mk1 = make_mask(nvalid, 1, half);
 
       // ---- window 0 of stage kt from F0; F1 <- window 1 of stage kt ----
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
         const int qx = m >> 2, qy = m & 3;
+        first_use(F0, m, mk0);
         acc[qy][qx] = mfma(F0[4 + qy], F0[qx], acc[qy][qx]);
-        if (m < 8) read(cs, 1, soff, nvalid, kOrder[m], F1[kOrder[m]]);
+        if (m < 8) read(cs, 1, soff, kOrder[m], F1[kOrder[m]]);
         MX_FENCE();
       }
       // ---- window 1 of stage kt from F1; F0 <- window 0 of stage kt+1;
@@ -449,13 +474,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
       static_for<0, 16>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
         constexpr int qx = m >> 2, qy = m & 3;
+        first_use(F1, m, mk1);
         acc[qy][qx] = mfma(F1[4 + qy], F1[qx], acc[qy][qx]);
         if constexpr (m < 8) {   // two loads per MFMA up front
           issue_load<2 * m>(pend, L, wv, lane);
           issue_load<2 * m + 1>(pend, L, wv, lane);
         }
         if constexpr (m == 8) issue_load<16>(pend, L, wv, lane);
-        if constexpr (m < 8) read(nst, 0, soff_n, nvalid_n, kOrder[m], F0[kOrder[m]]);
+        if constexpr (m < 8) read(nst, 0, soff_n, kOrder[m], F0[kOrder[m]]);
         MX_FENCE();
       });
     }
