@@ -426,47 +426,47 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
     // is read: an LDS wait right after each read would stall the MFMAs the
     // read is meant to overlap
     auto first_use = [&](Frag* F, int m, const WinMask& mk) {
-      if (MODE == 1) {
-        const int qx = m >> 2, qy = m & 3;
-        if (qx == 0) mask_frag(F[4 + qy], mk);
-        if (qy == 0) mask_frag(F[qx], mk);
-      }
+      const int qx = m >> 2, qy = m & 3;
+      if (qx == 0) mask_frag(F[4 + qy], mk);
+      if (qy == 0) mask_frag(F[qx], mk);
     };
     // refill order: what the next window's first MFMAs need comes first
     constexpr int kOrder[8] = {0, 4, 5, 6, 7, 1, 2, 3};
 
-    {
-      const StageDma d0 = make_stage_dma(smem, 0, L, k0, 0, ns, wv);
-      issue_loads<0, 17>(d0, L, wv, lane);
-      const StageDma d1 = make_stage_dma(smem, 1, L, k0, 1, ns, wv);
-      issue_loads<0, 17>(d1, L, wv, lane);
-    }
-    asm volatile("s_waitcnt vmcnt(17) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stage 0 has landed
-    {
-      const int soff = (int)((k0 >> 5) & 3);
-#pragma unroll
-      for (int f = 0; f < 8; ++f) read(smem, 0, soff, f, F0[f]);
-    }
-    for (int kt = 0; kt < ns; ++kt) {
+    // One stage.  NXS = X sub-tiles of this wave that hold rows of the tile
+    // (a group's last M-tile may be partial: MFMAs and fragment reads of
+    // sub-tiles past its end are not compiled in); MASK = the stage has
+    // contraction blocks outside the wgrad group.  Each variant is one
+    // straight-line block, so its schedule is the one written here.
+    auto stage = [&](auto nxs_c, auto mask_c, int kt) __attribute__((always_inline)) {
+      constexpr int NXS = decltype(nxs_c)::value;
+      constexpr bool MASK = decltype(mask_c)::value;
       const int buf = kt & 1;
       const uint8_t* cs = smem + buf * kStageBytes;           // this stage
       const uint8_t* nst = smem + (buf ^ 1) * kStageBytes;    // next stage
       const int64_t kk = k0 + (int64_t)kt * kBK;
       const int soff = (int)((kk >> 5) & 3);
-      const int64_t kn = kk + kBK;
-      const int soff_n = (int)((kn >> 5) & 3);
-      const int nvalid = MODE == 1 ? stage_valid(kk, k_lo, k1) : 0;
-      const WinMask mk0 = make_mask(nvalid, 0, half), mk1 = make_mask(nvalid, 1, half);
-
-      // ---- window 0 of stage kt from F0; F1 <- window 1 of stage kt ----
-#pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        const int qx = m >> 2, qy = m & 3;
-        first_use(F0, m, mk0);
-        acc[qy][qx] = mfma(F0[4 + qy], F0[qx], acc[qy][qx]);
-        if (m < 8) read(cs, 1, soff, kOrder[m], F1[kOrder[m]]);
-        MX_FENCE();
+      const int soff_n = (int)(((kk + kBK) >> 5) & 3);
+      WinMask mk0{}, mk1{};
+      if (MASK) {
+        const int nvalid = stage_valid(kk, k_lo, k1);
+        mk0 = make_mask(nvalid, 0, half);
+        mk1 = make_mask(nvalid, 1, half);
       }
+      // ---- window 0 of stage kt from F0; F1 <- window 1 of stage kt ----
+      static_for<0, 16>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        constexpr int qx = m >> 2, qy = m & 3;
+        if constexpr (qx < NXS) {
+          if constexpr (MASK) first_use(F0, m, mk0);
+          acc[qy][qx] = mfma(F0[4 + qy], F0[qx], acc[qy][qx]);
+        }
+        if constexpr (m < 8) {
+          constexpr int f = kOrder[m];
+          if constexpr (f < 4 ? f < NXS : NXS > 0) read(cs, 1, soff, f, F1[f]);
+        }
+        MX_FENCE();
+      });
       // ---- window 1 of stage kt from F1; F0 <- window 0 of stage kt+1;
       // ---- DMA of stage kt+2 into this stage's buffer ----
       stage_barrier();   // stage kt+1 landed; every wave is done reading buffer `buf`
@@ -474,17 +474,61 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
       static_for<0, 16>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
         constexpr int qx = m >> 2, qy = m & 3;
-        first_use(F1, m, mk1);
-        acc[qy][qx] = mfma(F1[4 + qy], F1[qx], acc[qy][qx]);
+        if constexpr (qx < NXS) {
+          if constexpr (MASK) first_use(F1, m, mk1);
+          acc[qy][qx] = mfma(F1[4 + qy], F1[qx], acc[qy][qx]);
+        }
         if constexpr (m < 8) {   // two loads per MFMA up front
           issue_load<2 * m>(pend, L, wv, lane);
           issue_load<2 * m + 1>(pend, L, wv, lane);
         }
         if constexpr (m == 8) issue_load<16>(pend, L, wv, lane);
-        if constexpr (m < 8) read(nst, 0, soff_n, kOrder[m], F0[kOrder[m]]);
+        if constexpr (m < 8) {
+          constexpr int f = kOrder[m];
+          if constexpr (f < 4 ? f < NXS : NXS > 0) read(nst, 0, soff_n, f, F0[f]);
+        }
         MX_FENCE();
       });
-    }
+    };
+
+    auto run = [&](auto nxs_c) __attribute__((always_inline)) {
+      constexpr int NXS = decltype(nxs_c)::value;
+      {
+        const StageDma d0 = make_stage_dma(smem, 0, L, k0, 0, ns, wv);
+        issue_loads<0, 17>(d0, L, wv, lane);
+        const StageDma d1 = make_stage_dma(smem, 1, L, k0, 1, ns, wv);
+        issue_loads<0, 17>(d1, L, wv, lane);
+      }
+      asm volatile("s_waitcnt vmcnt(17) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stage 0 has landed
+      {
+        const int soff = (int)((k0 >> 5) & 3);
+        static_for<0, 8>([&](auto fc) {
+          constexpr int f = decltype(fc)::value;
+          if constexpr (f < 4 ? f < NXS : NXS > 0) read(smem, 0, soff, f, F0[f]);
+        });
+      }
+      if (MODE == 1) {
+        // only a wgrad tile's first and last stage can hold blocks outside
+        // its group (stages are whole 128-byte lines of the group's span)
+        stage(nxs_c, std::true_type{}, 0);
+        for (int kt = 1; kt < ns - 1; ++kt) stage(nxs_c, std::false_type{}, kt);
+        if (ns > 1) stage(nxs_c, std::true_type{}, ns - 1);
+      } else {
+        for (int kt = 0; kt < ns; ++kt) stage(nxs_c, std::false_type{}, kt);
+      }
+    };
+    // X sub-tiles of this wave inside the tile (mode 1 tiles are whole in X)
+    const int nxs = MODE == 0 ? (int)min(max((rows_x - iw * 128 + 31) >> 5, (int64_t)0), (int64_t)4) : 4;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
+    if (MODE == 1 || nxs >= 4) run(I4{});
+    else if (nxs == 3) run(I3{});
+    else if (nxs == 2) run(I2{});
+    else if (nxs == 1) run(I1{});
+    else run(I0{});
     // drain the empty-range loads still in flight before the workgroup ends
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
