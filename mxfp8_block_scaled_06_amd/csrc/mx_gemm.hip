@@ -570,13 +570,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int qy = 0; qy < 4; ++qy) {
         const v16f& v = acc[qy][qx];
+        // register group g holds columns 8g + 4*half + 0..3.  Trading groups
+        // with the partner lane l ^ 32 (group 0 of the upper half for group 1
+        // of the lower, 2 for 3) leaves each lane 8 consecutive columns,
+        // 8*half + 16p + 0..7 for p = 0, 1: two 16-byte LDS writes, which
+        // with the 528-byte row pitch hit all banks once per 8 lanes.
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = jw * 128 + qy * 32 + 8 * g + 4 * half;
-          v2i w;
-          w[0] = (int)pack_bf16x2_rne(v[4 * g + 0], v[4 * g + 1]);
-          w[1] = (int)pack_bf16x2_rne(v[4 * g + 2], v[4 * g + 3]);
-          *(v2i*)(ot + row * kOutPitch + col * 2) = w;
+        for (int pr = 0; pr < 2; ++pr) {
+          const int g0 = 2 * pr, g1 = 2 * pr + 1;
+          const unsigned a0 = pack_bf16x2_rne(v[4 * g0 + 0], v[4 * g0 + 1]);
+          const unsigned a1 = pack_bf16x2_rne(v[4 * g0 + 2], v[4 * g0 + 3]);
+          const unsigned b0 = pack_bf16x2_rne(v[4 * g1 + 0], v[4 * g1 + 1]);
+          const unsigned b1 = pack_bf16x2_rne(v[4 * g1 + 2], v[4 * g1 + 3]);
+          // lanes < 32 get (own group g0, partner's g0); lanes >= 32 get
+          // (partner's g1, own g1)
+          const auto x = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+          const auto y = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+          const v4i w = {(int)x[0], (int)y[0], (int)x[1], (int)y[1]};
+          const int col = jw * 128 + qy * 32 + 16 * pr + 8 * half;
+          *(v4i*)(ot + row * kOutPitch + col * 2) = w;
         }
         __builtin_amdgcn_sched_barrier(0);
       }

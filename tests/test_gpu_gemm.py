@@ -8,6 +8,8 @@ sigma/16 so outputs near zero are judged on the output's scale, plus the
 dot-product error bound of the MFMA's internal summation.  The bf16 output
 must also equal the round-to-nearest-even of the fp32 output bit for bit."""
 
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -185,11 +187,19 @@ def test_gemm_deterministic_and_errors():
 _CACHE = {}
 
 
+def _workload(name):
+    # "<name>_pad32": the workload with every group padded to a multiple of 32
+    # (the wgrad contract), e.g. the skewed DeepSeek-style routing
+    if name.endswith("_pad32"):
+        return dataclasses.replace(inp.WORKLOADS[name[:-6]], pad32=True)
+    return inp.WORKLOADS[name]
+
+
 def _inputs(name, with_grad=False):
     key = (name, with_grad)
     if key not in _CACHE:
         _CACHE.clear()
-        _CACHE[key] = inp.make_inputs(name, with_grad=with_grad)
+        _CACHE[key] = inp.make_inputs(_workload(name), with_grad=with_grad)
     return _CACHE[key]
 
 
@@ -225,7 +235,7 @@ def test_fwd_full_size_sampled(name):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["llama4_bwd", "debug_shard"])
+@pytest.mark.parametrize("name", ["llama4_bwd", "debug_shard", "deepseek_share"])
 def test_dgrad_full_size_sampled(name):
     require_gpu()
     x = _inputs(name, with_grad=True)
@@ -244,7 +254,7 @@ def test_dgrad_full_size_sampled(name):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["llama4_bwd", "debug_shard"])
+@pytest.mark.parametrize("name", ["llama4_bwd", "debug_shard", "deepseek_share_pad32"])
 def test_wgrad_full_size_sampled(name):
     torch = require_gpu()
     import mxfp8_block_scaled_06_amd as mx
