@@ -144,19 +144,26 @@ __device__ __forceinline__ TileDesc decode_tile(const GemmArgs& a, int* s_offs, 
     if (b >= t8) return d;
     const int64_t t = (b & 7) * (t8 / 8) + (b >> 3);     // XCD-contiguous slice
     if (t >= total) return d;
+    // Inside a band of `width` N-tiles, expert e owns positions
+    // [pref[e] * width, pref[e+1] * width): its N-tiles in turn, and for each
+    // all of its M-tiles, so the workgroups running together on an XCD
+    // cover whole experts and each weight row panel is fetched once.
     const int64_t band = t / (total_m * kBand);
     const int64_t within = t - band * total_m * kBand;
     const int64_t width = min((int64_t)kBand, ntj - band * kBand);
-    const int64_t mt = within / width;
-    const int64_t nt = band * kBand + within % width;
-    // expert owning M-tile mt: the last e with pref[e] <= mt (experts without
+    const int64_t mw = within / width;
+    // expert owning M-tile mw: the last e with pref[e] <= mw (experts without
     // tiles share their successor's prefix and are skipped by this rule)
     int lo = 0, hi = a.E - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (s_pref[mid] <= mt) lo = mid; else hi = mid - 1;
+      if (s_pref[mid] <= mw) lo = mid; else hi = mid - 1;
     }
     const int e = lo;
+    const int64_t cnt = (e + 1 < a.E ? (int64_t)s_pref[e + 1] : total_m) - s_pref[e];
+    const int64_t r = within - (int64_t)s_pref[e] * width;
+    const int64_t mt = s_pref[e] + r % cnt;
+    const int64_t nt = band * kBand + r / cnt;
     int64_t st = e == 0 ? 0 : s_offs[e - 1];
     int64_t en = s_offs[e];
     st = min(max(st, (int64_t)0), a.I);
