@@ -18,8 +18,10 @@
 //    the lane supplies covers 32-element block l/32 of the window.  The
 //    accumulator of lane l holds column l%32 and rows 8(r/4) + 4(l/32) + r%4.
 //  * The A operand of the MFMA is Y and the B operand is X, so each lane's
-//    accumulators hold four consecutive output columns of one output row:
-//    the bf16 epilogue writes 8-byte runs without an LDS round trip.
+//    accumulators hold runs of four consecutive output columns of one output
+//    row; trading runs with lane l ^ 32 gives 8-column (16-byte) pieces,
+//    which the bf16 epilogue stages through the idle LDS so the global
+//    stores write whole 512-byte row segments.
 //  * Workgroup tile 256 x 256, 4 waves of 128 x 128 (4x4 MFMA tiles each,
 //    256 fp32 accumulators per lane in AGPRs).  Stages of 128 contraction
 //    bytes: every row moves as one full 128-byte line, HBM/L2 -> LDS by
@@ -40,12 +42,18 @@
 //    the longest latency budget), and the next stage has landed.
 //  * Tile scheduler on the device: the group offsets never cross to the host.
 //    Mode 0 enumerates (expert, M-tile) pairs from the offsets; tiles are
-//    ordered in bands of 8 N-tiles so concurrently running workgroups share
-//    operand rows, and the workgroup id is remapped so each XCD (workgroups
-//    are dealt round-robin over the 8 XCDs) receives a contiguous slice of the
-//    tile order, keeping the shared rows in that XCD's L2.
-//  * K blocks past the end of a wgrad group are zeroed in registers with a
-//    neutral scale; empty wgrad groups store zeros.
+//    ordered in bands of 8 N-tiles, expert by expert inside a band with all
+//    of an expert's M-tiles together per N-tile, so concurrently running
+//    workgroups share operand rows; the workgroup id is remapped so each XCD
+//    (workgroups are dealt round-robin over the 8 XCDs) receives a
+//    contiguous slice of the tile order, keeping the shared rows in that
+//    XCD's L2.
+//  * The stage loop is compiled per case and each variant is one straight
+//    block: a group's last, partial M-tile runs a loop without the MFMAs and
+//    fragment reads of the 32-row X sub-tiles past the group end.
+//  * K blocks outside a wgrad group are zeroed in registers with a neutral
+//    scale, at a fragment's first use and only in a tile's first and last
+//    stage; empty wgrad groups store zeros.
 #include "mx_device.h"
 #include "mx_kernels.h"
 
