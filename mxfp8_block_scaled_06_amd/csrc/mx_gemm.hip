@@ -234,10 +234,11 @@ struct LoadState {
 
 // DMA of one stage (contraction bytes [k0 + 128*stage_no, +128)) into LDS
 // buffer `buf`: per wave 8 + 8 one-KiB data loads (rows 64*wv .. +63 of X and
-// Y) and one 1 KiB scale chunk (wave 0/1: X chunks q, q+1; wave 2/3: Y chunks
-// q, q+1; chunk q+1 only when the stage is not 4-block aligned).  Stages at or
-// past `ns` get empty ranges: no data moves, but every wave still issues its
-// 17 loads so the vmcnt bookkeeping is the same for every stage.
+// Y) and one scale load: stages start on a multiple of 128 bytes, so a
+// stage's scales are the single 1 KiB chunk q = kk / 128 per operand, loaded
+// by wave 0 (X) and wave 2 (Y); waves 1 and 3 issue an empty load.  Stages at
+// or past `ns` get empty ranges: no data moves, but every wave still issues
+// its 17 loads so the vmcnt bookkeeping is the same for every stage.
 struct StageDma {
   __amdgpu_buffer_rsrc_t rx, ry, rs;
   uint8_t* st;
@@ -251,9 +252,8 @@ __device__ __forceinline__ StageDma make_stage_dma(uint8_t* smem, int buf, const
   const int64_t kk = k0 + (int64_t)stage_no * kBK;
   d.rx = make_rsrc(L.xb + kk, live ? L.x_bytes - kk : 0);
   d.ry = make_rsrc(L.yb + kk, live ? L.y_bytes - kk : 0);
-  const int64_t kb = kk >> 5;
-  const int64_t q = (kb >> 2) + (wv & 1);
-  const bool need = live && q < L.nchunks && ((wv & 1) == 0 || (kb & 3) != 0);
+  const int64_t q = kk / kBK;
+  const bool need = live && q < L.nchunks && (wv & 1) == 0;
   const bool is_x = wv < 2;
   const uint8_t* sbase = is_x ? L.sxb + q * L.sx_chunk : L.syb + q * L.sy_chunk;
   d.rs = make_rsrc(sbase, need ? (is_x ? L.sx_rows4 : L.sy_rows4) : 0);
@@ -296,14 +296,12 @@ struct Frag {
 
 // Read the operand of one 32-row sub-tile (this lane's `row`) for MFMA window
 // `w` (0/1) of a stage: pieces 4w + half and 4w + half + 2 of the row, and
-// the scale byte of block 2w + half.  `soff` = byte offset of the stage's
-// first block inside the staged scale chunks (0..3).
+// the scale byte of block 2w + half from the stage's [rows][4] scale chunk.
 __device__ __forceinline__ void read_frag(const uint8_t* tile, const uint8_t* sc, int row, int pa, int pb, int w,
-                                          int half, int soff, Frag& f) {
+                                          int half, Frag& f) {
   const v4i a0 = *(const v4i*)(tile + row * kBK + pa);
   const v4i a1 = *(const v4i*)(tile + row * kBK + pb);
-  const int t = soff + 2 * w + half;
-  f.s = sc[(t >> 2) * kScaleChunk + row * 4 + (t & 3)];
+  f.s = sc[row * 4 + 2 * w + half];
   f.v = (v8i){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
 }
 
@@ -429,12 +427,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
     // read has a whole window of MFMAs to land.
     Frag F0[8], F1[8];
     // fragment `f` of window `w` of the stage in LDS buffer `st`
-    auto read = [&](const uint8_t* st, int w, int soffv, int f, Frag& dst) {
+    auto read = [&](const uint8_t* st, int w, int f, Frag& dst) {
       if (f < 4) {
-        read_frag(st, st + 2 * kTileBytes, xrow0 + 32 * f, pc[w][0], pc[w][1], w, half, soffv, dst);
+        read_frag(st, st + 2 * kTileBytes, xrow0 + 32 * f, pc[w][0], pc[w][1], w, half, dst);
       } else {
         read_frag(st + kTileBytes, st + 2 * kTileBytes + 2 * kScaleChunk, yrow0 + 32 * (f - 4), pc[w][0], pc[w][1], w,
-                  half, soffv, dst);
+                  half, dst);
       }
     };
     // wgrad masking is applied where a fragment is first used, not where it
@@ -460,8 +458,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
       const uint8_t* cs = smem + buf * kStageBytes;           // this stage
       const uint8_t* nst = smem + (buf ^ 1) * kStageBytes;    // next stage
       const int64_t kk = k0 + (int64_t)kt * kBK;
-      const int soff = (int)((kk >> 5) & 3);
-      const int soff_n = (int)(((kk + kBK) >> 5) & 3);
       WinMask mk0{}, mk1{};
       if (MASK) {
         const int nvalid = stage_valid(kk, k_lo, k1);
@@ -478,7 +474,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
         }
         if constexpr (m < 8) {
           constexpr int f = kOrder[m];
-          if constexpr (f < 4 ? f < NXS : NXS > 0) read(cs, 1, soff, f, F1[f]);
+          if constexpr (f < 4 ? f < NXS : NXS > 0) read(cs, 1, f, F1[f]);
         }
         MX_FENCE();
       });
@@ -500,7 +496,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
         if constexpr (m == 8) issue_load<16>(pend, L, wv, lane);
         if constexpr (m < 8) {
           constexpr int f = kOrder[m];
-          if constexpr (f < 4 ? f < NXS : NXS > 0) read(nst, 0, soff_n, f, F0[f]);
+          if constexpr (f < 4 ? f < NXS : NXS > 0) read(nst, 0, f, F0[f]);
         }
         MX_FENCE();
       });
@@ -515,13 +511,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
         issue_loads<0, 17>(d1, L, wv, lane);
       }
       asm volatile("s_waitcnt vmcnt(17) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stage 0 has landed
-      {
-        const int soff = (int)((k0 >> 5) & 3);
-        static_for<0, 8>([&](auto fc) {
-          constexpr int f = decltype(fc)::value;
-          if constexpr (f < 4 ? f < NXS : NXS > 0) read(smem, 0, soff, f, F0[f]);
-        });
-      }
+      static_for<0, 8>([&](auto fc) {
+        constexpr int f = decltype(fc)::value;
+        if constexpr (f < 4 ? f < NXS : NXS > 0) read(smem, 0, f, F0[f]);
+      });
       if (MODE == 1) {
         // only a wgrad tile's first and last stage can hold blocks outside
         // its group (stages are whole 128-byte lines of the group's span)
