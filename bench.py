@@ -6,14 +6,17 @@ routed top-1 by a uniform multinomial, K=5120, N=8192, groups padded with
 zero rows to multiples of 32):
     weights  W -> both MX orientations in one pass (mx_quantize_weights; the
              weights change once per optimizer step)
-    forward  out = A @ W[e]^T      (quantize A rowwise, grouped GEMM)
-    dgrad    dA  = dOut @ W[e]     (quantize dOut rowwise, GEMM on W's
-                                    colwise orientation)
-    wgrad    dW  = dOut^T @ A      (quantize dOut and A along tokens, GEMM)
-through the library's entry points, so every quantize kernel, the tile
-scheduler, the GEMM main loop and the bf16 epilogue run in the step.  The
-same step through the three all-bf16 entry points (weights quantized twice)
-is timed too and reported as `step_bf16_entry_points_ms`.
+    forward  out = A @ W[e]^T      (A -> both orientations in one pass, grouped
+                                    GEMM on the rowwise one)
+    dgrad    dA  = dOut @ W[e]     (dOut -> both orientations in one pass,
+                                    GEMM on W's colwise orientation)
+    wgrad    dW  = dOut^T @ A      (GEMM on the token-blocked orientations of
+                                    dOut and A quantized above)
+as the differentiable primitive composes it, so the quantize kernels, the
+tile scheduler, the GEMM main loop and the bf16 epilogue all run in the step.
+The same step through the three all-bf16 entry points (weights quantized
+twice, each activation quantized once per GEMM) is timed too and reported as
+`step_bf16_entry_points_ms`.
 
 Printed: one JSON line.  `value` = algorithmic GEMM TFLOP/s of the whole
 step (2*M*N*K per GEMM on the real tokens, quantization time included).
@@ -159,11 +162,21 @@ def main():
     dA = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     dW = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
     ws = {op: torch.empty(mx.mx_grouped_mm_workspace_bytes(op, M, N, K, E), dtype=torch.uint8, device=dev)
-          for op in (mx.OP_FWD_Q, mx.OP_DGRAD_Q, mx.OP_WGRAD)}
+          for op in (mx.OP_WGRAD,)}
     wq = (torch.empty((E, N, K), dtype=torch.uint8, device=dev),
           torch.empty((E, K // 128, N, 4), dtype=torch.uint8, device=dev),
           torch.empty((E, K, N), dtype=torch.uint8, device=dev),
           torch.empty((E, N // 128, K, 4), dtype=torch.uint8, device=dev))
+    # activations in both orientations; the token axis of the transposed
+    # orientation is padded to a multiple of 128 (the wgrad contraction)
+    Mq = (M + 127) // 128 * 128
+
+    def dual_bufs(cols):
+        return (torch.empty((M, cols), dtype=torch.uint8, device=dev),
+                torch.empty((cols // 128, M, 4), dtype=torch.uint8, device=dev),
+                torch.empty((cols, Mq), dtype=torch.uint8, device=dev),
+                torch.empty((Mq // 128, cols, 4), dtype=torch.uint8, device=dev))
+    aq, gq = dual_bufs(K), dual_bufs(N)
 
     def step(ev=None):
         if ev is not None:
@@ -171,13 +184,15 @@ def main():
         qW, sW, qWt, sWt = mx.mx_quantize_weights(W, *wq)
         if ev is not None:
             ev[1].record()
-        mx.mx_grouped_mm_fwd_q(A, qW, sW, offs, out=out, ws=ws[mx.OP_FWD_Q])
+        qA, sA, qAt, sAt = mx.mx_quantize_dual(A, Mq, *aq)
+        mx.mx_grouped_gemm_mx(qA, sA, qW, sW, offs, 0, out=out)
         if ev is not None:
             ev[2].record()
-        mx.mx_grouped_mm_dgrad_q(G, qWt, sWt, offs, out=dA, ws=ws[mx.OP_DGRAD_Q])
+        qG, sG, qGt, sGt = mx.mx_quantize_dual(G, Mq, *gq)
+        mx.mx_grouped_gemm_mx(qG, sG, qWt, sWt, offs, 0, out=dA)
         if ev is not None:
             ev[3].record()
-        mx.mx_grouped_mm_wgrad(G, A, offs, out=dW, ws=ws[mx.OP_WGRAD])
+        mx.mx_grouped_gemm_mx(qGt, sGt, qAt, sAt, offs, 1, out=dW)
         if ev is not None:
             ev[4].record()
 
@@ -275,12 +290,18 @@ def main():
         qt = torch.empty((C, R), dtype=torch.uint8, device=dev)
         s_col = torch.empty((C, R // 32), dtype=torch.uint8, device=dev)
         s_sq = torch.empty((R // 32, C // 32), dtype=torch.uint8, device=dev)
+        Rq = (R + 127) // 128 * 128
+        dq = (q, torch.empty((C // 128, R, 4), dtype=torch.uint8, device=dev),
+              torch.empty((C, Rq), dtype=torch.uint8, device=dev),
+              torch.empty((Rq // 128, C, 4), dtype=torch.uint8, device=dev))
         for name, fn, nbytes in (
                 ("weights_both_orientations", lambda: mx.mx_quantize_weights(W, *wq),
                  E * N * K * 4 + 2 * E * N * K // 32),
                 ("rowwise", lambda: mx.mx_quantize_rowwise(X, q, s_row), 3 * R * C + R * C // 32),
                 ("colwise", lambda: mx.mx_quantize_colwise(X, qt, s_col), 3 * R * C + R * C // 32),
-                ("32x32", lambda: mx.mx_quantize_32x32(X, q, s_sq), 3 * R * C + R * C // 1024)):
+                ("32x32", lambda: mx.mx_quantize_32x32(X, q, s_sq), 3 * R * C + R * C // 1024),
+                ("rowwise_and_colwise_one_pass", lambda: mx.mx_quantize_dual(X, Rq, *dq),
+                 4 * R * C + 2 * R * C // 32)):
             fn()
             torch.cuda.synchronize()
             t = time_launches(torch, fn, args.reps)
@@ -288,7 +309,7 @@ def main():
             quant[name] = {"ms": t["mean_ms"], "GB_s": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS,
                            "bytes": nbytes}
             log(f"quant {name}: {t['mean_ms']:.3f} ms  {gbs:.0f} GB/s  {100 * gbs / PEAK_HBM_GBS:.1f}%")
-        del X, q, s_row, qt, s_col, s_sq
+        del X, q, s_row, qt, s_col, s_sq, dq
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

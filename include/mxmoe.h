@@ -211,6 +211,24 @@ mx_status mx_quantize_rowwise_gather(const uint16_t* x, int64_t src_rows, const 
 mx_status mx_quantize_weights(const uint16_t* w, int64_t E, int64_t N, int64_t K, uint8_t* q, uint8_t* s,
                               uint8_t* q_t, uint8_t* s_t, void* stream);
 
+/* Activations in both orientations from one read: the forward quantizes its
+ * tokens A [M, K] 1x32 along K for its own GEMM and 32x1 along the tokens for
+ * the wgrad GEMM of the backward; the backward does the same with dOut [M, N]
+ * for dgrad and wgrad ("MXFP8 training for MoEs": the backward mirrors the
+ * forward, with each GEMM's operands blocked along its contraction dim).
+ * x [rows, cols] bf16 -> q [rows, cols] (1x32 blocks along cols) with s in the
+ * GEMM scale layout [cols/128, rows, 4] (X of the rows-grouped GEMM), and
+ * q_t [cols, ldq] (32x1 blocks along rows, stored transposed) with s_t in the
+ * GEMM scale layout [ldq/128, cols, 4] (an operand of the wgrad GEMM with
+ * Kc = ldq).  Columns rows .. ldq-1 of q_t are the codes of zero rows (0x00,
+ * scale byte 0).  Requires rows % 32 == 0, cols % 128 == 0, ldq % 128 == 0
+ * and ldq >= rows.  Over rows 0 .. rows-1, bit-identical to
+ * mx_quantize_rowwise and mx_quantize_colwise followed by
+ * mx_scales_to_gemm_layout.  x, q, q_t 16-byte aligned; s, s_t 4-byte
+ * aligned. */
+mx_status mx_quantize_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldq, uint8_t* q, uint8_t* s,
+                           uint8_t* q_t, uint8_t* s_t, void* stream);
+
 /* Workspaces of the two entry points below (they quantize only the
  * activation side). */
 #define MX_OP_FWD_Q 3

@@ -19,7 +19,9 @@ __all__ = [
     "mx_quantize_rowwise", "mx_quantize_colwise", "mx_quantize_32x32",
     "mx_grouped_gemm_mx", "mx_grouped_gemm_mx_f32", "mx_grouped_mm_workspace_bytes", "mx_scales_to_gemm_layout",
     "mx_grouped_mm_fwd", "mx_grouped_mm_dgrad", "mx_grouped_mm_wgrad",
-    "OP_FWD", "OP_DGRAD", "OP_WGRAD",
+    "mx_quantize_weights", "mx_quantize_dual", "mx_quantize_rowwise_gather",
+    "mx_grouped_mm_fwd_q", "mx_grouped_mm_dgrad_q", "mx_grouped_mm", "mx_linear",
+    "OP_FWD", "OP_DGRAD", "OP_WGRAD", "OP_FWD_Q", "OP_DGRAD_Q",
 ]
 
 OP_FWD, OP_DGRAD, OP_WGRAD, OP_FWD_Q, OP_DGRAD_Q = 0, 1, 2, 3, 4
@@ -74,6 +76,8 @@ def load_library():
     lib.mx_quantize_rowwise_gather.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp]
     lib.mx_quantize_weights.restype = c_int
     lib.mx_quantize_weights.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]
+    lib.mx_quantize_dual.restype = c_int
+    lib.mx_quantize_dual.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]
     for name in ("mx_grouped_mm_fwd_q", "mx_grouped_mm_dgrad_q"):
         f = getattr(lib, name)
         f.restype = c_int
@@ -112,6 +116,21 @@ def _require(t, dtype, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _out(t, shape, dtype, device, name):
+    """An output buffer: allocated when None, else checked to be exactly what
+    the kernel writes (the C ABI sees only a pointer and cannot)."""
+    import torch
+    shape = tuple(int(d) for d in shape)
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if isinstance(t, torch.Tensor) and tuple(t.shape) != shape:
+        raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+    _require(t, dtype, name)
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    return t
+
+
 def _as3d(x):
     if x.dim() == 2:
         return 1, x.shape[0], x.shape[1]
@@ -130,10 +149,8 @@ def mx_quantize_rowwise(x, q=None, s=None) -> Tuple["torch.Tensor", "torch.Tenso
     _require(x, torch.bfloat16, "x")
     B, R, C = _as3d(x)
     lead = x.shape[:-1]
-    if q is None:
-        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    if s is None:
-        s = torch.empty((*lead, C // 32 if C % 32 == 0 else 0), dtype=torch.uint8, device=x.device)
+    q = _out(q, x.shape, torch.uint8, x.device, "q")
+    s = _out(s, (*lead, C // 32 if C % 32 == 0 else 0), torch.uint8, x.device, "s")
     _check("mx_quantize_rowwise", lib.mx_quantize_rowwise(_ptr(x), B, R, C, _ptr(q), _ptr(s), _stream(x.device)))
     return q, s
 
@@ -146,10 +163,8 @@ def mx_quantize_colwise(x, q_t=None, s_t=None):
     _require(x, torch.bfloat16, "x")
     B, R, C = _as3d(x)
     lead = x.shape[:-2]
-    if q_t is None:
-        q_t = torch.empty((*lead, C, R), dtype=torch.uint8, device=x.device)
-    if s_t is None:
-        s_t = torch.empty((*lead, C, R // 32 if R % 32 == 0 else 0), dtype=torch.uint8, device=x.device)
+    q_t = _out(q_t, (*lead, C, R), torch.uint8, x.device, "q_t")
+    s_t = _out(s_t, (*lead, C, R // 32 if R % 32 == 0 else 0), torch.uint8, x.device, "s_t")
     _check("mx_quantize_colwise",
            lib.mx_quantize_colwise(_ptr(x), B, R, C, _ptr(q_t), _ptr(s_t), _stream(x.device)))
     return q_t, s_t
@@ -162,10 +177,8 @@ def mx_quantize_32x32(x, q=None, s=None):
     _require(x, torch.bfloat16, "x")
     B, R, C = _as3d(x)
     lead = x.shape[:-2]
-    if q is None:
-        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    if s is None:
-        s = torch.empty((*lead, R // 32, C // 32), dtype=torch.uint8, device=x.device)
+    q = _out(q, x.shape, torch.uint8, x.device, "q")
+    s = _out(s, (*lead, R // 32, C // 32), torch.uint8, x.device, "s")
     _check("mx_quantize_32x32", lib.mx_quantize_32x32(_ptr(x), B, R, C, _ptr(q), _ptr(s), _stream(x.device)))
     return q, s
 
@@ -176,8 +189,7 @@ def mx_scales_to_gemm_layout(s, out=None):
     lib = load_library()
     _require(s, torch.uint8, "s")
     B, R, KB = _as3d(s)
-    if out is None:
-        out = torch.empty((*s.shape[:-2], KB // 4, R, 4), dtype=torch.uint8, device=s.device)
+    out = _out(out, (*s.shape[:-2], KB // 4, R, 4), torch.uint8, s.device, "out")
     _check("mx_scales_to_gemm_layout",
            lib.mx_scales_to_gemm_layout(_ptr(s), B, R, KB, _ptr(out), _stream(s.device)))
     return out
@@ -201,12 +213,25 @@ def mx_grouped_gemm_mx(X, sX, Y, sY, offs, mode: int, out=None, out_dtype=None):
         _require(t, torch.uint8, n)
     _require(offs, torch.int32, "offs")
     E = offs.shape[0]
+    if X.dim() != 2:
+        raise ValueError("X must be [I, Kc]")
     I, Kc = X.shape
-    J = Y.shape[1] if mode == 0 else Y.shape[0]
-    if out is None:
-        shape = (I, J) if mode == 0 else (E, I, J)
-        out = torch.empty(shape, dtype=out_dtype, device=X.device)
-    _require(out, out_dtype, "out")
+    if mode == 0:
+        if Y.dim() != 3 or Y.shape[0] != E or Y.shape[2] != Kc:
+            raise ValueError(f"mode 0: Y must be [E={E}, J, Kc={Kc}], got {tuple(Y.shape)}")
+        J = Y.shape[1]
+        y_rows = E * J
+    else:
+        if Y.dim() != 2 or Y.shape[1] != Kc:
+            raise ValueError(f"mode 1: Y must be [J, Kc={Kc}], got {tuple(Y.shape)}")
+        J = Y.shape[0]
+        y_rows = J
+    # scales hold one byte per 32 contraction bytes of every operand row (any
+    # arrangement of that size: row-major or the GEMM layout)
+    if sX.numel() != I * (Kc // 32) or sY.numel() != y_rows * (Kc // 32):
+        raise ValueError(f"sX / sY must hold {I * (Kc // 32)} / {y_rows * (Kc // 32)} bytes, "
+                         f"got {sX.numel()} / {sY.numel()}")
+    out = _out(out, (I, J) if mode == 0 else (E, I, J), out_dtype, X.device, "out")
     name = "mx_grouped_gemm_mx" if out_dtype == torch.bfloat16 else "mx_grouped_gemm_mx_f32"
     _check(name, getattr(lib, name)(_ptr(X), _ptr(sX), _ptr(Y), _ptr(sY), _ptr(offs), mode, I, J, Kc, E,
                                     _ptr(out), _stream(X.device)))
@@ -221,6 +246,14 @@ def mx_grouped_gemm_mx_f32(X, sX, Y, sY, offs, mode: int, out=None):
 
 def mx_grouped_mm_workspace_bytes(op: int, M: int, N: int, K: int, E: int) -> int:
     return int(load_library().mx_grouped_mm_workspace_bytes(op, M, N, K, E))
+
+
+def _offs(offs, E):
+    """offs: int32 [E] group END offsets on the GPU (the kernels read E entries)."""
+    import torch
+    if isinstance(offs, torch.Tensor) and (offs.dim() != 1 or offs.shape[0] != E):
+        raise ValueError(f"offs must be int32 [{E}] (one END offset per expert), got {tuple(offs.shape)}")
+    _require(offs, torch.int32, "offs")
 
 
 def _ws(op, M, N, K, E, device, ws):
@@ -245,8 +278,8 @@ def mx_grouped_mm_fwd(A, W, offs, out=None, ws=None):
     E, N, K2 = W.shape
     if K2 != K:
         raise ValueError(f"A has K={K} but W has K={K2}")
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _offs(offs, E)
+    out = _out(out, (M, N), torch.bfloat16, A.device, "out")
     ws = _ws(OP_FWD, M, N, K, E, A.device, ws)
     _check("mx_grouped_mm_fwd",
            lib.mx_grouped_mm_fwd(_ptr(A), _ptr(W), _ptr(offs), M, N, K, E, _ptr(out), _ptr(ws), ws.numel(),
@@ -265,8 +298,8 @@ def mx_grouped_mm_dgrad(dOut, W, offs, out=None, ws=None):
     E, N2, K = W.shape
     if N2 != N:
         raise ValueError(f"dOut has N={N} but W has N={N2}")
-    if out is None:
-        out = torch.empty((M, K), dtype=torch.bfloat16, device=dOut.device)
+    _offs(offs, E)
+    out = _out(out, (M, K), torch.bfloat16, dOut.device, "out")
     ws = _ws(OP_DGRAD, M, N, K, E, dOut.device, ws)
     _check("mx_grouped_mm_dgrad",
            lib.mx_grouped_mm_dgrad(_ptr(dOut), _ptr(W), _ptr(offs), M, N, K, E, _ptr(out), _ptr(ws), ws.numel(),
@@ -286,8 +319,7 @@ def mx_grouped_mm_wgrad(dOut, A, offs, out=None, ws=None):
     if M2 != M:
         raise ValueError(f"dOut has M={M} but A has M={M2}")
     E = offs.shape[0]
-    if out is None:
-        out = torch.empty((E, N, K), dtype=torch.bfloat16, device=A.device)
+    out = _out(out, (E, N, K), torch.bfloat16, A.device, "out")
     ws = _ws(OP_WGRAD, M, N, K, E, A.device, ws)
     _check("mx_grouped_mm_wgrad",
            lib.mx_grouped_mm_wgrad(_ptr(dOut), _ptr(A), _ptr(offs), M, N, K, E, _ptr(out), _ptr(ws), ws.numel(),
@@ -309,16 +341,35 @@ def mx_quantize_weights(W, q=None, s=None, q_t=None, s_t=None):
         raise ValueError("W must be [E, N, K]")
     E, N, K = W.shape
     dev = W.device
-    if q is None:
-        q = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
-    if s is None:
-        s = torch.empty((E, K // 128, N, 4), dtype=torch.uint8, device=dev)
-    if q_t is None:
-        q_t = torch.empty((E, K, N), dtype=torch.uint8, device=dev)
-    if s_t is None:
-        s_t = torch.empty((E, N // 128, K, 4), dtype=torch.uint8, device=dev)
+    q = _out(q, (E, N, K), torch.uint8, dev, "q")
+    s = _out(s, (E, K // 128, N, 4), torch.uint8, dev, "s")
+    q_t = _out(q_t, (E, K, N), torch.uint8, dev, "q_t")
+    s_t = _out(s_t, (E, N // 128, K, 4), torch.uint8, dev, "s_t")
     _check("mx_quantize_weights", lib.mx_quantize_weights(_ptr(W), E, N, K, _ptr(q), _ptr(s), _ptr(q_t), _ptr(s_t),
                                                           _stream(dev)))
+    return q, s, q_t, s_t
+
+
+def mx_quantize_dual(x, ldq: Optional[int] = None, q=None, s=None, q_t=None, s_t=None):
+    """Activations x bf16 [rows, cols] in both orientations from one read:
+    (q [rows, cols], s [cols/128, rows, 4]) = X of the rows-grouped GEMM, and
+    (q_t [cols, ldq], s_t [ldq/128, cols, 4]) = a wgrad operand with Kc = ldq
+    (default: rows rounded up to 128; the padding columns are zero codes)."""
+    import torch
+    lib = load_library()
+    _require(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, cols]")
+    rows, cols = x.shape
+    if ldq is None:
+        ldq = (rows + 127) // 128 * 128
+    dev = x.device
+    q = _out(q, (rows, cols), torch.uint8, dev, "q")
+    s = _out(s, (cols // 128, rows, 4), torch.uint8, dev, "s")
+    q_t = _out(q_t, (cols, ldq), torch.uint8, dev, "q_t")
+    s_t = _out(s_t, (ldq // 128, cols, 4), torch.uint8, dev, "s_t")
+    _check("mx_quantize_dual", lib.mx_quantize_dual(_ptr(x), rows, cols, ldq, _ptr(q), _ptr(s), _ptr(q_t), _ptr(s_t),
+                                                    _stream(dev)))
     return q, s, q_t, s_t
 
 
@@ -334,8 +385,10 @@ def mx_grouped_mm_fwd_q(A, qW, sW, offs, out=None, ws=None):
     E, N, K2 = qW.shape
     if K2 != K:
         raise ValueError(f"A has K={K} but qW has K={K2}")
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _offs(offs, E)
+    if sW.numel() != E * N * (K // 32):
+        raise ValueError(f"sW must hold E*N*K/32 = {E * N * (K // 32)} bytes, got {sW.numel()}")
+    out = _out(out, (M, N), torch.bfloat16, A.device, "out")
     ws = _ws(OP_FWD_Q, M, N, K, E, A.device, ws)
     _check("mx_grouped_mm_fwd_q",
            lib.mx_grouped_mm_fwd_q(_ptr(A), _ptr(qW), _ptr(sW), _ptr(offs), M, N, K, E, _ptr(out), _ptr(ws),
@@ -355,8 +408,10 @@ def mx_grouped_mm_dgrad_q(dOut, qWt, sWt, offs, out=None, ws=None):
     E, K, N2 = qWt.shape
     if N2 != N:
         raise ValueError(f"dOut has N={N} but qWt has N={N2}")
-    if out is None:
-        out = torch.empty((M, K), dtype=torch.bfloat16, device=dOut.device)
+    _offs(offs, E)
+    if sWt.numel() != E * K * (N // 32):
+        raise ValueError(f"sWt must hold E*K*N/32 = {E * K * (N // 32)} bytes, got {sWt.numel()}")
+    out = _out(out, (M, K), torch.bfloat16, dOut.device, "out")
     ws = _ws(OP_DGRAD_Q, M, N, K, E, dOut.device, ws)
     _check("mx_grouped_mm_dgrad_q",
            lib.mx_grouped_mm_dgrad_q(_ptr(dOut), _ptr(qWt), _ptr(sWt), _ptr(offs), M, N, K, E, _ptr(out), _ptr(ws),
@@ -385,10 +440,8 @@ def mx_quantize_rowwise_gather(x, rows, q=None, s=None):
     _require(rows, torch.int32, "rows")
     src_rows, cols = x.shape
     M = rows.shape[0]
-    if q is None:
-        q = torch.empty((M, cols), dtype=torch.uint8, device=x.device)
-    if s is None:
-        s = torch.empty((cols // 128, M, 4), dtype=torch.uint8, device=x.device)
+    q = _out(q, (M, cols), torch.uint8, x.device, "q")
+    s = _out(s, (cols // 128, M, 4), torch.uint8, x.device, "s")
     _check("mx_quantize_rowwise_gather",
            lib.mx_quantize_rowwise_gather(_ptr(x), src_rows, _ptr(rows), M, cols, _ptr(q), _ptr(s), _stream(x.device)))
     return q, s

@@ -8,8 +8,12 @@ grouped GEMM, result in the original precision, differentiable; section "Why
 Does MXFP8 Speed Up MoE Training So Much?": the backward mirrors the forward).
 The forward quantizes the expert weights once in both orientations and keeps
 the one the backward needs: the weight 4-tuple of the MoK expert PR review.
-Every step runs in the library's kernels; this module only wires them into
-torch.autograd.
+Activations get the same treatment: the forward quantizes A in both
+orientations from one read (1x32 along K for its own GEMM, 32x1 along the
+tokens for the wgrad GEMM) and keeps the fp8 transpose instead of the bf16 A;
+the backward quantizes dOut in both orientations (dgrad and wgrad) from one
+read.  Every step runs in the library's kernels; this module only wires them
+into torch.autograd.
 
 Contract (checked here, with a clear error otherwise):
   A    bf16 [M, K] tokens grouped by expert (offs: int32 [E] END offsets on
@@ -22,7 +26,8 @@ Contract (checked here, with a clear error otherwise):
 
 from __future__ import annotations
 
-from . import (mx_grouped_mm_dgrad_q, mx_grouped_mm_fwd_q, mx_grouped_mm_wgrad, mx_quantize_weights)
+from . import (mx_grouped_gemm_mx, mx_grouped_mm_dgrad_q, mx_grouped_mm_fwd_q, mx_quantize_dual,
+               mx_quantize_weights)
 
 
 def _check(A, W, offs):
@@ -58,22 +63,35 @@ class _MXGroupedMM:
                 @staticmethod
                 def forward(ctx, A, W, offs):
                     qW, sW, qWt, sWt = mx_quantize_weights(W)
-                    out = mx_grouped_mm_fwd_q(A, qW, sW, offs)
-                    # the forward orientation is not needed again; the backward
+                    if ctx.needs_input_grad[1]:
+                        # A in both orientations: the 32x1-along-tokens codes
+                        # are the wgrad operand, kept instead of the bf16 A
+                        qA, sA, qAt, sAt = mx_quantize_dual(A)
+                        out = mx_grouped_gemm_mx(qA, sA, qW, sW, offs, 0)
+                        del qA, sA
+                    else:
+                        out = mx_grouped_mm_fwd_q(A, qW, sW, offs)
+                        qAt = sAt = None
+                    # the forward orientation of W is not needed again; the backward
                     # keeps the 32x1-along-N codes (weight_t_fp8 / weight_t_scale)
                     del qW, sW
-                    ctx.save_for_backward(A, offs, qWt, sWt)
+                    ctx.save_for_backward(offs, qWt, sWt, qAt, sAt)
                     return out
 
                 @staticmethod
                 def backward(ctx, dOut):
-                    A, offs, qWt, sWt = ctx.saved_tensors
+                    offs, qWt, sWt, qAt, sAt = ctx.saved_tensors
                     dOut = dOut.contiguous()
                     dA = dW = None
-                    if ctx.needs_input_grad[0]:
-                        dA = mx_grouped_mm_dgrad_q(dOut, qWt, sWt, offs)
                     if ctx.needs_input_grad[1]:
-                        dW = mx_grouped_mm_wgrad(dOut, A, offs)
+                        # dOut in both orientations from one read: 1x32 along N
+                        # for dgrad, 32x1 along the tokens for wgrad
+                        qG, sG, qGt, sGt = mx_quantize_dual(dOut, ldq=qAt.shape[1])
+                        if ctx.needs_input_grad[0]:
+                            dA = mx_grouped_gemm_mx(qG, sG, qWt, sWt, offs, 0)
+                        dW = mx_grouped_gemm_mx(qGt, sGt, qAt, sAt, offs, 1)
+                    elif ctx.needs_input_grad[0]:
+                        dA = mx_grouped_mm_dgrad_q(dOut, qWt, sWt, offs)
                     return dA, dW, None
 
             cls.fn = Fn

@@ -315,7 +315,26 @@ mx_status mx_quantize_weights(const uint16_t* w, int64_t E, int64_t N, int64_t K
   if (!w || !q || !s || !q_t || !s_t) return fail(MX_ERR_NULL, "%s: null pointer", fn);
   if (!aligned(w, 16) || !aligned(q, 16) || !aligned(q_t, 16) || !aligned(s, 4) || !aligned(s_t, 4))
     return fail(MX_ERR_ALIGN, "%s: w, q, q_t must be 16-byte and s, s_t 4-byte aligned", fn);
-  return hip_status(mxk::launch_quant_dual(w, E, N, K, q, s, q_t, s_t, (hipStream_t)stream), fn);
+  return hip_status(mxk::launch_quant_dual(w, E, N, K, N, q, s, q_t, s_t, (hipStream_t)stream), fn);
+}
+
+mx_status mx_quantize_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldq, uint8_t* q, uint8_t* s,
+                           uint8_t* q_t, uint8_t* s_t, void* stream) {
+  const char* fn = "mx_quantize_dual";
+  if (rows < 0 || cols < 0 || ldq < 0)
+    return fail(MX_ERR_SHAPE, "%s: rows=%lld cols=%lld ldq=%lld", fn, (long long)rows, (long long)cols, (long long)ldq);
+  if (rows % 32 != 0 || cols % 128 != 0)
+    return fail(MX_ERR_SHAPE, "%s: rows=%lld must be a multiple of 32 and cols=%lld of 128", fn, (long long)rows,
+                (long long)cols);
+  if (ldq % 128 != 0 || ldq < rows)
+    return fail(MX_ERR_SHAPE, "%s: ldq=%lld must be a multiple of 128 and >= rows=%lld", fn, (long long)ldq,
+                (long long)rows);
+  if (ldq == 0 || cols == 0) return MX_OK;
+  if (ldq / 128 > 65535 || cols / 128 > 65535) return fail(MX_ERR_SHAPE, "%s: too large for one launch", fn);
+  if (!x || !q || !s || !q_t || !s_t) return fail(MX_ERR_NULL, "%s: null pointer", fn);
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(q_t, 16) || !aligned(s, 4) || !aligned(s_t, 4))
+    return fail(MX_ERR_ALIGN, "%s: x, q, q_t must be 16-byte and s, s_t 4-byte aligned", fn);
+  return hip_status(mxk::launch_quant_dual(x, 1, rows, cols, ldq, q, s, q_t, s_t, (hipStream_t)stream), fn);
 }
 
 mx_status mx_grouped_mm_fwd_q(const uint16_t* A, const uint8_t* qW, const uint8_t* sW, const int32_t* offs, int64_t M,

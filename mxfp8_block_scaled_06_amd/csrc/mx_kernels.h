@@ -37,11 +37,11 @@ hipError_t launch_quant_rowwise_gather(const uint16_t* x, int64_t src_rows, cons
 // gemm_layout == 0: s_t [batch][cols][lds]; 1: GEMM layout [batch][ldq/128][cols][4].
 hipError_t launch_quant_colwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q_t,
                                 int64_t ldq, uint8_t* s_t, int64_t lds, int gemm_layout, hipStream_t st);
-// Both orientations of w [E, N, K] (N % 128 == 0, K % 128 == 0): q [E, N, K]
-// with s in GEMM layout [E][K/128][N][4]; q_t [E, K, N] with s_t in GEMM
-// layout [E][N/128][K][4].
-hipError_t launch_quant_dual(const uint16_t* w, int64_t E, int64_t N, int64_t K, uint8_t* q, uint8_t* s,
-                             uint8_t* q_t, uint8_t* s_t, hipStream_t st);
+// Both orientations of w [E, N, K] (N % 32 == 0, K % 128 == 0, ldq % 128 == 0,
+// ldq >= N): q [E, N, K] with s in GEMM layout [E][K/128][N][4]; q_t
+// [E, K, ldq] with s_t in GEMM layout [E][ldq/128][K][4], zero past N.
+hipError_t launch_quant_dual(const uint16_t* w, int64_t E, int64_t N, int64_t K, int64_t ldq, uint8_t* q,
+                             uint8_t* s, uint8_t* q_t, uint8_t* s_t, hipStream_t st);
 hipError_t launch_scales_to_gemm(const uint8_t* s, int64_t batch, int64_t rows, int64_t kb, uint8_t* out,
                                  hipStream_t st);
 hipError_t launch_quant_32x32(const uint16_t* x, int64_t rows_total, int64_t cols, uint8_t* q, uint8_t* s,

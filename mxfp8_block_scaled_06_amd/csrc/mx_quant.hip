@@ -229,10 +229,14 @@ __global__ __launch_bounds__(256) void quant_colwise_kernel(const uint16_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// Both orientations of expert weights in one pass: w [E, N, K] ->
-//   q   [E, N, K] (1x32 blocks along K), s   GEMM layout [E][K/128][N][4]
-//   q_t [E, K, N] (32x1 blocks along N), s_t GEMM layout [E][N/128][K][4]
-// (N % 128 == 0, K % 128 == 0).  A workgroup stages a 128 (n) x 128 (k) bf16
+// Both orientations in one pass: w [E, N, K] ->
+//   q   [E, N, K]   (1x32 blocks along K), s   GEMM layout [E][K/128][N][4]
+//   q_t [E, K, ldq] (32x1 blocks along N), s_t GEMM layout [E][ldq/128][K][4]
+// (K % 128 == 0, N % 32 == 0, ldq % 128 == 0, ldq >= N; rows [N, ldq) are
+// quantized as zero rows, so q_t's padding columns hold zero codes and zero
+// scales).  Expert weights use ldq = N; activations (the forward's A, the
+// backward's dOut) use ldq = N rounded up to 128, the contraction length of
+// the wgrad GEMM.  A workgroup stages a 128 (n) x 128 (k) bf16
 // tile in LDS once; the rowwise half quantizes its rows straight to q (four
 // threads fill one 128-byte line), the colwise half is the colwise kernel's
 // path (column pairs, codes transposed back through LDS for whole-line
@@ -244,19 +248,21 @@ __global__ __launch_bounds__(256) void quant_colwise_kernel(const uint16_t* __re
 constexpr int kDualPitch = 272;   // bytes per staged input row (256 + 16): conflict-free row and column reads
 
 __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restrict__ w, int64_t N, int64_t K,
-                                                         uint8_t* __restrict__ q, uint8_t* __restrict__ s,
-                                                         uint8_t* __restrict__ q_t, uint8_t* __restrict__ s_t) {
+                                                         int64_t ldq, uint8_t* __restrict__ q,
+                                                         uint8_t* __restrict__ s, uint8_t* __restrict__ q_t,
+                                                         uint8_t* __restrict__ s_t) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kColTile * kDualPitch];
   const int tid = threadIdx.x;
   const int64_t b = blockIdx.z;
-  const int64_t n0 = (int64_t)blockIdx.y * kColTile;
+  const int64_t n0 = (int64_t)blockIdx.y * kColTile;   // ldq % 128 == 0: rows [N, ldq) read as zeros
   const int64_t k0 = (int64_t)blockIdx.x * kColTile;
   const uint16_t* wb = w + b * N * K;
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
     const int chunk = it * 256 + tid;
     const int rr = chunk >> 4, cc = chunk & 15;
-    const v4i v = __builtin_nontemporal_load((const v4i*)(wb + (n0 + rr) * K + k0 + cc * 8));
+    v4i v = (v4i){0, 0, 0, 0};
+    if (n0 + rr < N) v = __builtin_nontemporal_load((const v4i*)(wb + (n0 + rr) * K + k0 + cc * 8));
     *(v4i*)(tile + rr * kDualPitch + cc * 16) = v;
   }
   __syncthreads();
@@ -283,11 +289,13 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
       o0 = (v4i){c0[0], c0[1], c1[0], c1[1]};
       o1 = (v4i){c2[0], c2[1], c3[0], c3[1]};
     }
-    uint8_t* qp = q + (b * N + n0 + row) * K + k0 + blk * 32;
-    *(v4i*)qp = o0;
-    *(v4i*)(qp + 16) = o1;
-    // [E][K/128][N][4]: the tile's 128 columns are one chunk
-    s[b * (K / 32) * N + (k0 >> 7) * N * 4 + (n0 + row) * 4 + blk] = (uint8_t)byte;
+    if (n0 + row < N) {
+      uint8_t* qp = q + (b * N + n0 + row) * K + k0 + blk * 32;
+      *(v4i*)qp = o0;
+      *(v4i*)(qp + 16) = o1;
+      // [E][K/128][N][4]: the tile's 128 columns are one chunk
+      s[b * (K / 32) * N + (k0 >> 7) * N * 4 + (n0 + row) * 4 + blk] = (uint8_t)byte;
+    }
   }
 
   // ---- colwise: wave w quantizes rows [32w, 32w+32) of columns 2l, 2l+1
@@ -332,11 +340,11 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
     const int p = j * 256 + tid;
     const int orow = p >> 3, pc = p & 7;
     const v4i x = *(const v4i*)(o8 + orow * kColPitch + 16 * pc);
-    *(v4i*)(q_t + (b * K + k0 + orow) * N + n0 + 16 * pc) = x;
+    *(v4i*)(q_t + (b * K + k0 + orow) * ldq + n0 + 16 * pc) = x;
   }
   if (tid < kColTile) {
-    // [E][N/128][K][4]: blocks n0/32 .. n0/32 + 3 of output row k0 + tid
-    *(uint32_t*)(s_t + b * (N / 32) * K + (n0 >> 7) * K * 4 + (k0 + tid) * 4) = *(const uint32_t*)(sc + tid * 4);
+    // [E][ldq/128][K][4]: blocks n0/32 .. n0/32 + 3 of output row k0 + tid
+    *(uint32_t*)(s_t + b * (ldq / 32) * K + (n0 >> 7) * K * 4 + (k0 + tid) * 4) = *(const uint32_t*)(sc + tid * 4);
   }
 }
 
@@ -395,11 +403,11 @@ hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows_total, int64_t c
   return hipGetLastError();
 }
 
-hipError_t launch_quant_dual(const uint16_t* w, int64_t E, int64_t N, int64_t K, uint8_t* q, uint8_t* s,
-                             uint8_t* q_t, uint8_t* s_t, hipStream_t st) {
-  if (E == 0 || N == 0 || K == 0) return hipSuccess;
-  dim3 grid((unsigned)(K / kColTile), (unsigned)(N / kColTile), (unsigned)E);
-  hipLaunchKernelGGL(quant_dual_kernel, grid, dim3(256), 0, st, w, N, K, q, s, q_t, s_t);
+hipError_t launch_quant_dual(const uint16_t* w, int64_t E, int64_t N, int64_t K, int64_t ldq, uint8_t* q,
+                             uint8_t* s, uint8_t* q_t, uint8_t* s_t, hipStream_t st) {
+  if (E == 0 || ldq == 0 || K == 0) return hipSuccess;
+  dim3 grid((unsigned)(K / kColTile), (unsigned)(ldq / kColTile), (unsigned)E);
+  hipLaunchKernelGGL(quant_dual_kernel, grid, dim3(256), 0, st, w, N, K, ldq, q, s, q_t, s_t);
   return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     for n in ("mx_quantize_rowwise", "mx_quantize_colwise", "mx_quantize_32x32", "mx_grouped_mm_fwd",
               "mx_grouped_mm_dgrad", "mx_grouped_mm_wgrad", "mx_grouped_gemm_mx",
               "mx_grouped_mm_workspace_bytes", "mx_last_error", "mx_version", "mx_quantize_weights",
-              "mx_grouped_mm_fwd_q", "mx_grouped_mm_dgrad_q", "mx_quantize_rowwise_gather"):
+              "mx_grouped_mm_fwd_q", "mx_grouped_mm_dgrad_q", "mx_quantize_rowwise_gather", "mx_quantize_dual"):
         assert n in names
 
 
@@ -107,6 +107,31 @@ def test_prequantized_weight_entry_points_validate():
     d = lib.mx_grouped_mm_dgrad_q
     assert d(FAKE, FAKE, FAKE, FAKE, 256, 96, 64, 2, FAKE, FAKE, 1 << 40, None) == 2      # N % 128
     assert lib.mx_grouped_mm_workspace_bytes(4, 256, 512, 256, 2) >= 256 * 512 * 33 // 32
+
+
+def test_dual_quantize_validates():
+    lib = _lib()
+    d = lib.mx_quantize_dual
+    assert d(FAKE, 48, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == 2      # rows % 32
+    assert "multiple of 32" in _err(lib)
+    assert d(FAKE, 64, 96, 128, FAKE, FAKE, FAKE, FAKE, None) == 2       # cols % 128
+    assert d(FAKE, 160, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == 2     # ldq < rows
+    assert ">= rows" in _err(lib)
+    assert d(FAKE, 64, 128, 192, FAKE, FAKE, FAKE, FAKE, None) == 2      # ldq % 128
+    assert d(FAKE, 64, 128, 128, FAKE, FAKE, None, FAKE, None) == 1      # null q_t
+    assert d(FAKE, 64, 128, 128, FAKE + 8, FAKE, FAKE, FAKE, None) == 3  # misaligned q
+    assert d(None, 0, 128, 0, None, None, None, None, None) == 0         # nothing to do
+
+
+def test_binding_checks_caller_buffers_and_offsets():
+    """Output buffers and offsets given to the binding must be exactly what the
+    kernels write and read: the C ABI sees only pointers."""
+    import torch
+    _lib()
+    with pytest.raises(ValueError, match="must have shape"):
+        mx._out(torch.empty((3, 4), dtype=torch.uint8), (4, 4), torch.uint8, torch.device("cpu"), "q")
+    with pytest.raises(ValueError, match="one END offset per expert"):
+        mx._offs(torch.zeros(3, dtype=torch.int32), 4)
 
 
 def test_gather_quantize_validates():
