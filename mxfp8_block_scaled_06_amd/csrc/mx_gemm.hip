@@ -38,8 +38,8 @@
 //    and while one window's 16 MFMAs run the other set is refilled for the
 //    next window.  One barrier per stage, at the start of its second window:
 //    every wave has then finished reading the stage's buffer, which receives
-//    the DMA of the stage after next (issued two loads per MFMA up front, for
-//    the longest latency budget), and the next stage has landed.
+//    the DMA of the stage after next (issued one load per MFMA across the
+//    window), and the next stage has landed.
 //  * Tile scheduler on the device: the group offsets never cross to the host.
 //    Mode 0 enumerates (expert, M-tile) pairs from the offsets; tiles are
 //    ordered in bands of 8 N-tiles, expert by expert inside a band with all
@@ -489,11 +489,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
           if constexpr (MASK) first_use(F1, m, mk1);
           acc[qy][qx] = mfma(F1[4 + qy], F1[qx], acc[qy][qx]);
         }
-        if constexpr (m < 8) {   // two loads per MFMA up front
-          issue_load<2 * m>(pend, L, wv, lane);
-          issue_load<2 * m + 1>(pend, L, wv, lane);
-        }
-        if constexpr (m == 8) issue_load<16>(pend, L, wv, lane);
+        // one load per MFMA (the scale chunk with the first): the four
+        // waves' loads then arrive at the address unit about as fast as it
+        // takes them, and no wave stalls on a full queue in front of an MFMA
+        issue_load<m>(pend, L, wv, lane);
+        if constexpr (m == 0) issue_load<16>(pend, L, wv, lane);
         if constexpr (m < 8) {
           constexpr int f = kOrder[m];
           if constexpr (f < 4 ? f < NXS : NXS > 0) read(nst, 0, f, F0[f]);
