@@ -60,6 +60,9 @@ def parse():
     p.add_argument("--reps", type=int, default=10, help="launches per GEMM-only / quantize timing")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     p.add_argument("--no-quant-sweep", action="store_true")
+    p.add_argument("--vendor", action="store_true",
+                   help="also time hipBLASLt's GEMMs (through torch) and this library's GEMM on one dense "
+                        "GEMM of the forward's FLOPs (M=16384, N=8192, K=5120): a same-run vendor reference")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (HBM counter calibration for rocprofv3 --pmc)")
     return p.parse_args()
@@ -95,6 +98,49 @@ def traffic_for_current_kernel():
         return rec.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
         return None
+
+
+def vendor_reference(torch, mx, dev, reps):
+    """hipBLASLt (bf16 matmul, per-tensor-scaled FP8 and MXFP8 `torch._scaled_mm`)
+    and this library's MX GEMM (one expert, unit scales) on the same dense
+    GEMM: 16384 x 8192 x 5120, the forward's FLOPs as one matrix product.
+    Context for the roofline fraction; nothing here is on the library's path."""
+    M, N, K = 16384, 8192, 5120
+    flops = 2.0 * M * N * K
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    a16 = torch.randn((M, K), device=dev, generator=gen).to(torch.bfloat16)
+    w16 = torch.randn((N, K), device=dev, generator=gen).to(torch.bfloat16)
+    a8, w8 = a16.to(torch.float8_e4m3fn), w16.to(torch.float8_e4m3fn)
+    one = torch.ones((), device=dev)
+    unit = lambda r: torch.full((r, K // 32), 127, dtype=torch.uint8, device=dev).view(torch.float8_e8m0fnu)
+    sa, sb = unit(M), unit(N)
+    X, Y = a8.view(torch.uint8), w8.view(torch.uint8).view(1, N, K)
+    sX = torch.full((K // 128, M, 4), 127, dtype=torch.uint8, device=dev)
+    sY = torch.full((1, K // 128, N, 4), 127, dtype=torch.uint8, device=dev)
+    offs = torch.tensor([M], dtype=torch.int32, device=dev)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    cases = (
+        ("hipblaslt_bf16", lambda: torch.matmul(a16, w16.t()), 2500.0),
+        ("hipblaslt_fp8_per_tensor_scale",
+         lambda: torch._scaled_mm(a8, w8.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16), 5000.0),
+        ("hipblaslt_mxfp8", lambda: torch._scaled_mm(a8, w8.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16),
+         5000.0),
+        ("mxmoe_mxfp8_one_expert", lambda: mx.mx_grouped_gemm_mx(X, sX, Y, sY, offs, 0, out=c), 5000.0),
+    )
+    res = {"shape_MNK": [M, N, K]}
+    for name, fn, peak in cases:
+        try:
+            fn()
+            torch.cuda.synchronize()
+            t = time_launches(torch, fn, reps)
+            tf = flops / (t["mean_ms"] * 1e-3) / 1e12
+            res[name] = {"ms": t["mean_ms"], "tflops": tf, "frac_of_peak": tf / peak, "peak_tflops": peak}
+            log(f"vendor reference {name}: {t['mean_ms']:.3f} ms  {tf:.0f} TFLOP/s  {100 * tf / peak:.1f}% of peak")
+        except Exception as ex:   # an op this torch build lacks is reported, not fatal
+            res[name] = {"error": f"{type(ex).__name__}: {str(ex)[:200]}"}
+            log(f"vendor reference {name}: {res[name]['error']}")
+    return res
 
 
 def cpu_baseline(x, experts=8, rows_per_expert=128):
@@ -318,6 +364,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    vendor = None
+    if args.vendor:
+        vendor = vendor_reference(torch, mx, dev, args.reps)
+        torch.cuda.empty_cache()
+
     # ---------------- CPU oracle leg ----------------
     cpu = None
     if not args.no_cpu:
@@ -351,6 +402,7 @@ def main():
         "quant_sweep_65600x5120": quant,   # plus the [16, 8192, 5120] weights in both orientations
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "vendor_reference": vendor,
         "gpu": torch.cuda.get_device_name(0),
         "library": mx.version(),
     }
