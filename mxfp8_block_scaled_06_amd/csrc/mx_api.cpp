@@ -37,6 +37,10 @@ mx_status hip_status(hipError_t e, const char* what) {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// The rowwise quantizers index scale bytes with 32-bit integers: a launch
+// covers fewer than 2^32 blocks of 32 (about 256 GiB of bf16 input).
+bool rowwise_blocks_fit(int64_t rows, int64_t cols) { return rows * (cols / 32) < ((int64_t)1 << 32); }
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 // Checks shared by the quantizers.
@@ -124,6 +128,8 @@ mx_status mx_quantize_rowwise(const uint16_t* x, int64_t batch, int64_t rows, in
   mx_status st = check_quant("mx_quantize_rowwise", x, batch, rows, cols, q, s, 1, 32);
   if (st != MX_OK) return st;
   if (rows == 0 || cols == 0) return MX_OK;
+  if (!rowwise_blocks_fit(batch * rows, cols))
+    return fail(MX_ERR_SHAPE, "mx_quantize_rowwise: batch*rows*cols/32 must be below 2^32 blocks");
   return hip_status(mxk::launch_quant_rowwise(x, batch * rows, cols, q, s, 0, (hipStream_t)stream),
                     "mx_quantize_rowwise launch");
 }
@@ -264,6 +270,7 @@ mx_status mx_grouped_mm_dgrad(const uint16_t* dOut, const uint16_t* W, const int
   if (!aligned(ws, 256)) return fail(MX_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
   if (M == 0 || K == 0) return MX_OK;
   if ((N + 127) / 128 > 65535 || E > 65535) return fail(MX_ERR_SHAPE, "%s: N too large for one launch", fn);
+  if (!rowwise_blocks_fit(M, N)) return fail(MX_ERR_SHAPE, "%s: M*N/32 must be below 2^32 blocks", fn);
   uint8_t* w8 = (uint8_t*)ws;
   hipStream_t s = (hipStream_t)stream;
   uint8_t *qG = w8 + L.off[0], *sG = w8 + L.off[1], *qWt = w8 + L.off[2], *sWt = w8 + L.off[3];
@@ -351,6 +358,7 @@ mx_status mx_grouped_mm_fwd_q(const uint16_t* A, const uint8_t* qW, const uint8_
     return fail(MX_ERR_WORKSPACE, "%s: workspace of %zu bytes at %p, need %zu", fn, ws_bytes, ws, L.total);
   if (!aligned(ws, 256)) return fail(MX_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
   if (M == 0 || N == 0) return MX_OK;
+  if (!rowwise_blocks_fit(M, K)) return fail(MX_ERR_SHAPE, "%s: M*K/32 must be below 2^32 blocks", fn);
   uint8_t* w8 = (uint8_t*)ws;
   hipStream_t s = (hipStream_t)stream;
   uint8_t *qA = w8 + L.off[0], *sA = w8 + L.off[1];
@@ -372,6 +380,7 @@ mx_status mx_grouped_mm_dgrad_q(const uint16_t* dOut, const uint8_t* qWt, const 
     return fail(MX_ERR_WORKSPACE, "%s: workspace of %zu bytes at %p, need %zu", fn, ws_bytes, ws, L.total);
   if (!aligned(ws, 256)) return fail(MX_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
   if (M == 0 || K == 0) return MX_OK;
+  if (!rowwise_blocks_fit(M, N)) return fail(MX_ERR_SHAPE, "%s: M*N/32 must be below 2^32 blocks", fn);
   uint8_t* w8 = (uint8_t*)ws;
   hipStream_t s = (hipStream_t)stream;
   uint8_t *qG = w8 + L.off[0], *sG = w8 + L.off[1];
@@ -388,8 +397,8 @@ mx_status mx_quantize_rowwise_gather(const uint16_t* x, int64_t src_rows, const 
                 (long long)cols);
   if (cols % 128 != 0) return fail(MX_ERR_SHAPE, "%s: cols=%lld is not a multiple of 128", fn, (long long)cols);
   if (M == 0 || cols == 0) return MX_OK;
-  if (M * (cols / 8) >= ((int64_t)1 << 40) || M >= ((int64_t)1 << 31))
-    return fail(MX_ERR_SHAPE, "%s: too large", fn);
+  if (M >= ((int64_t)1 << 31) || !rowwise_blocks_fit(M, cols))
+    return fail(MX_ERR_SHAPE, "%s: too large (M < 2^31 rows and M*cols/32 < 2^32 blocks)", fn);
   if (!rows || !q || !s_gemm || (src_rows > 0 && !x)) return fail(MX_ERR_NULL, "%s: null pointer", fn);
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(rows, 4))
     return fail(MX_ERR_ALIGN, "%s: x and q must be 16-byte aligned, rows 4-byte aligned", fn);

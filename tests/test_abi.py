@@ -58,6 +58,10 @@ def test_quantize_validation_errors():
     assert lib.mx_quantize_rowwise(FAKE, 0, 4, 64, FAKE, FAKE, None) == 2
     assert lib.mx_quantize_rowwise(None, 1, 4, 64, FAKE, FAKE, None) == 1
     assert lib.mx_quantize_rowwise(FAKE + 8, 1, 4, 64, FAKE, FAKE, None) == 3
+    # 2^32 scale blocks: beyond the 32-bit scale indexing of the rowwise kernels
+    assert lib.mx_quantize_rowwise(FAKE, 1, 1 << 27, 1024, FAKE, FAKE, None) == 2
+    assert "2^32" in _err(lib)
+    assert lib.mx_quantize_rowwise(FAKE, 4, 1 << 25, 1024, FAKE, FAKE, None) == 2
     assert lib.mx_quantize_colwise(FAKE, 1, 48, 64, FAKE, FAKE, None) == 2
     assert lib.mx_quantize_colwise(FAKE, 1, 64, 12, FAKE, FAKE, None) == 2
     assert lib.mx_quantize_32x32(FAKE, 1, 64, 48, FAKE, FAKE, None) == 2
@@ -141,6 +145,7 @@ def test_gather_quantize_validates():
     assert g(FAKE, 10, None, 64, 128, FAKE, FAKE, None) == 1         # null rows
     assert g(FAKE + 8, 10, FAKE, 64, 128, FAKE, FAKE, None) == 3     # misaligned x
     assert g(None, 0, None, 0, 128, None, None, None) == 0            # nothing to do
+    assert g(FAKE, 10, FAKE, 1 << 26, 2048, FAKE, FAKE, None) == 2   # 2^32 scale blocks
 
 
 def test_workspace_sizes_cover_both_operands():
