@@ -63,6 +63,9 @@ def parse():
     p.add_argument("--vendor", action="store_true",
                    help="also time hipBLASLt's GEMMs (through torch) and this library's GEMM on one dense "
                         "GEMM of the forward's FLOPs (M=16384, N=8192, K=5120): a same-run vendor reference")
+    p.add_argument("--all-configs", action="store_true",
+                   help="also time the GEMM-only fwd/dgrad/wgrad on the debug-model shard (E=2, M=65600) and the "
+                        "DeepSeek-style share (E=32, Zipf routing) workloads, on their seeded inputs")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (HBM counter calibration for rocprofv3 --pmc)")
     return p.parse_args()
@@ -140,6 +143,56 @@ def vendor_reference(torch, mx, dev, reps):
         except Exception as ex:   # an op this torch build lacks is reported, not fatal
             res[name] = {"error": f"{type(ex).__name__}: {str(ex)[:200]}"}
             log(f"vendor reference {name}: {res[name]['error']}")
+    return res
+
+
+def other_configs(torch, mx, inp, dev, reps):
+    """GEMM-only timings on the other workloads: the debug-model shard (E=2,
+    M=65600 split 40/60, K=5120, N=8192; all three GEMMs) and the DeepSeek-style
+    share (E=32, M=32768, K=7168, N=2048, Zipf(1.2) routing with 2 empty
+    experts; the forward on the routed tokens, dgrad and wgrad with every group
+    padded to 32 rows).  Operands are the seeded inputs quantized by the
+    library as in the step (weights both ways, activations both ways)."""
+    import dataclasses
+    res = {}
+    cases = (("debug_shard", inp.WORKLOADS["debug_shard"], ("fwd", "dgrad", "wgrad")),
+             ("deepseek_share", inp.WORKLOADS["deepseek_share"], ("fwd",)),
+             ("deepseek_share_pad32", dataclasses.replace(inp.WORKLOADS["deepseek_share"], pad32=True),
+              ("dgrad", "wgrad")))
+    for name, w, ops in cases:
+        x = inp.make_inputs(w, with_grad=any(o != "fwd" for o in ops))
+        E, N, K = x.W.shape
+        M = x.M_rows
+        Mq = (M + 127) // 128 * 128
+        A = dev_bf16(torch, x.A, dev)
+        W = dev_bf16(torch, x.W, dev)
+        offs = torch.from_numpy(x.offs).to(dev)
+        qW, sW, qWt, sWt = mx.mx_quantize_weights(W)
+        del W
+        qA, sA, qAt, sAt = mx.mx_quantize_dual(A, Mq)
+        del A
+        if x.dOut is not None:
+            G = dev_bf16(torch, x.dOut, dev)
+            qG, sG, qGt, sGt = mx.mx_quantize_dual(G, Mq)
+            del G
+        flops = 2.0 * M * N * K
+        fns = {"fwd": lambda: mx.mx_grouped_gemm_mx(qA, sA, qW, sW, offs, 0),
+               "dgrad": lambda: mx.mx_grouped_gemm_mx(qG, sG, qWt, sWt, offs, 0),
+               "wgrad": lambda: mx.mx_grouped_gemm_mx(qGt, sGt, qAt, sAt, offs, 1)}
+        res[name] = {"E": E, "rows": M, "tokens": int(x.counts.sum()), "K": K, "N": N,
+                     "counts_min_max": [int(x.counts.min()), int(x.counts.max())]}
+        for op in ops:
+            fns[op]()
+            torch.cuda.synchronize()
+            t = time_launches(torch, fns[op], reps)
+            tf = flops / (t["mean_ms"] * 1e-3) / 1e12
+            res[name][op] = {"ms": t["mean_ms"], "tflops": tf, "frac_of_peak": tf / PEAK_MXFP8_TFLOPS,
+                             "flops_per_launch": flops}
+            log(f"{name} gemm-only {op}: {t['mean_ms']:.3f} ms  {tf:.1f} TFLOP/s  "
+                f"{100 * tf / PEAK_MXFP8_TFLOPS:.1f}% of peak")
+        del fns, qA, sA, qAt, sAt, qW, sW, qWt, sWt, offs
+        qG = sG = qGt = sGt = None
+        torch.cuda.empty_cache()
     return res
 
 
@@ -364,6 +417,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    more = None
+    if args.all_configs:
+        more = other_configs(torch, mx, inp, dev, args.reps)
+
     vendor = None
     if args.vendor:
         vendor = vendor_reference(torch, mx, dev, args.reps)
@@ -403,6 +460,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "vendor_reference": vendor,
+        "other_workloads_gemm_only": more,
         "gpu": torch.cuda.get_device_name(0),
         "library": mx.version(),
     }

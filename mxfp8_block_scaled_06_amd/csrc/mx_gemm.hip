@@ -66,6 +66,7 @@ constexpr int kBN = 256;        // output cols per tile (rows of Y)
 constexpr int kBK = 128;        // contraction bytes per stage (4 scale blocks, 2 MFMA windows)
 constexpr int kThreads = 256;   // 4 waves, 2 x 2 arrangement of 128 x 128
 constexpr int kBand = 8;        // N-tiles per band in the tile order
+constexpr int kWgChunk = 8;     // wgrad tiles per chunk dealt to one XCD
 constexpr int kTileBytes = kBM * kBK;             // 32 KiB per operand tile
 constexpr int kScaleChunk = kBM * 4;              // one [rows][4] scale chunk: 1 KiB
 constexpr int kStageBytes = 2 * kTileBytes + 4 * kScaleChunk;
@@ -188,10 +189,15 @@ __device__ __forceinline__ TileDesc decode_tile(const GemmArgs& a, int* s_offs, 
     const int64_t nti = (a.I + kBM - 1) / kBM;
     const int64_t per_e = nti * ntj;
     const int64_t total = per_e * a.E;
-    const int64_t t8 = (total + 7) / 8 * 8;
+    // A tile's work grows with its expert's token count, so whole experts
+    // per XCD would leave the XCD holding the largest group of a skewed
+    // routing with most of the work.  Chunks of kWgChunk consecutive tiles
+    // (a band row: the same X rows, consecutive Y rows) are dealt round-robin
+    // over the 8 XCDs instead; workgroup b runs on XCD b % 8, and that XCD's
+    // i-th workgroup takes tile i % kWgChunk of its (i / kWgChunk)-th chunk.
     const int64_t b = blockIdx.x;
-    if (b >= t8) return d;
-    const int64_t t = (b & 7) * (t8 / 8) + (b >> 3);
+    const int64_t i = b >> 3;
+    const int64_t t = ((i / kWgChunk) * 8 + (b & 7)) * kWgChunk + i % kWgChunk;
     if (t >= total) return d;
     const int e = (int)(t / per_e);
     const int64_t r = t - e * per_e;
@@ -628,7 +634,10 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t st) {
   } else {
     tiles = (a.I + kBM - 1) / kBM * ntj * a.E;
   }
-  const int64_t grid = (tiles + 7) / 8 * 8;
+  // mode 1 deals chunks of kWgChunk tiles round-robin over the 8 XCDs: every
+  // XCD gets as many workgroups as the XCD with the most chunks needs
+  const int64_t grid = a.mode == 0 ? (tiles + 7) / 8 * 8
+                                   : ((tiles + kWgChunk - 1) / kWgChunk + 7) / 8 * 8 * kWgChunk;
   if (tiles == 0) return hipSuccess;
   const size_t lds = gemm_lds_bytes();
   const void* fn;
