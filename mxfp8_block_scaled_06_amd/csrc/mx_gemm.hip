@@ -47,7 +47,9 @@
 //    workgroups share operand rows; the workgroup id is remapped so each XCD
 //    (workgroups are dealt round-robin over the 8 XCDs) receives a
 //    contiguous slice of the tile order, keeping the shared rows in that
-//    XCD's L2.
+//    XCD's L2.  In mode 1 a tile's work follows its expert's token count,
+//    so chunks of 8 tiles (one band row) are dealt round-robin over the XCDs
+//    instead: a skewed routing then loads every XCD alike.
 //  * The stage loop is compiled per case and each variant is one straight
 //    block: a group's last, partial M-tile runs a loop without the MFMAs and
 //    fragment reads of the 32-row X sub-tiles past the group end.
