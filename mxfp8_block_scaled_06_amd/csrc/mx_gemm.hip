@@ -44,12 +44,11 @@
 //    Mode 0 enumerates (expert, M-tile) pairs from the offsets; tiles are
 //    ordered in bands of 8 N-tiles, expert by expert inside a band with all
 //    of an expert's M-tiles together per N-tile, so concurrently running
-//    workgroups share operand rows; the workgroup id is remapped so each XCD
-//    (workgroups are dealt round-robin over the 8 XCDs) receives a
-//    contiguous slice of the tile order, keeping the shared rows in that
-//    XCD's L2.  In mode 1 a tile's work follows its expert's token count,
-//    so chunks of 8 tiles (one band row) are dealt round-robin over the XCDs
-//    instead: a skewed routing then loads every XCD alike.
+//    workgroups share operand rows.  Workgroups are dealt round-robin over
+//    the 8 XCDs by the hardware; the workgroup id is remapped so that chunks
+//    of 16 consecutive tiles of the order land on one XCD (its L2 sees their
+//    shared rows) and successive chunks go to successive XCDs, so every XCD
+//    gets a slice of every expert however the tokens are routed.
 //  * The stage loop is compiled per case and each variant is one straight
 //    block: a group's last, partial M-tile runs a loop without the MFMAs and
 //    fragment reads of the 32-row X sub-tiles past the group end.
@@ -68,7 +67,7 @@ constexpr int kBN = 256;        // output cols per tile (rows of Y)
 constexpr int kBK = 128;        // contraction bytes per stage (4 scale blocks, 2 MFMA windows)
 constexpr int kThreads = 256;   // 4 waves, 2 x 2 arrangement of 128 x 128
 constexpr int kBand = 8;        // N-tiles per band in the tile order
-constexpr int kWgChunk = 8;     // wgrad tiles per chunk dealt to one XCD
+constexpr int kXcdChunk = 16;   // consecutive tiles of the order dealt to one XCD at a time
 constexpr int kTileBytes = kBM * kBK;             // 32 KiB per operand tile
 constexpr int kScaleChunk = kBM * 4;              // one [rows][4] scale chunk: 1 KiB
 constexpr int kStageBytes = 2 * kTileBytes + 4 * kScaleChunk;
@@ -134,6 +133,19 @@ __device__ int scan_mtiles(const int* s_offs, int E, int64_t I, int* pref) {
   return carry;
 }
 
+// Position in the tile order of workgroup b.  The hardware deals workgroups
+// round-robin over the 8 XCDs (b % 8); that XCD's i-th workgroup (i = b / 8)
+// takes tile i % kXcdChunk of the XCD's (i / kXcdChunk)-th chunk, and chunks
+// of kXcdChunk consecutive tiles go round-robin to the XCDs.  Neighbouring
+// tiles of the order (one expert's M-tiles of an N-tile, or one band row)
+// share an XCD and its L2, while every XCD gets a slice of every expert: tile
+// costs differ (a group's partial last M-tile; in wgrad, the group size), and
+// whole experts per XCD left the XCDs unevenly loaded.
+__device__ __forceinline__ int64_t tile_of_workgroup(int64_t b) {
+  const int64_t i = b >> 3;
+  return ((i / kXcdChunk) * 8 + (b & 7)) * kXcdChunk + i % kXcdChunk;
+}
+
 template <int MODE>
 __device__ __forceinline__ TileDesc decode_tile(const GemmArgs& a, int* s_offs, int* s_pref, int* s_misc) {
   TileDesc d;
@@ -150,15 +162,12 @@ __device__ __forceinline__ TileDesc decode_tile(const GemmArgs& a, int* s_offs, 
     __syncthreads();
     const int64_t total_m = s_misc[0];
     const int64_t total = total_m * ntj;
-    const int64_t t8 = (total + 7) / 8 * 8;
-    const int64_t b = blockIdx.x;
-    if (b >= t8) return d;
-    const int64_t t = (b & 7) * (t8 / 8) + (b >> 3);     // XCD-contiguous slice
+    const int64_t t = tile_of_workgroup(blockIdx.x);
     if (t >= total) return d;
     // Inside a band of `width` N-tiles, expert e owns positions
     // [pref[e] * width, pref[e+1] * width): its N-tiles in turn, and for each
-    // all of its M-tiles, so the workgroups running together on an XCD
-    // cover whole experts and each weight row panel is fetched once.
+    // all of its M-tiles, so consecutive tiles (one XCD chunk) share a weight
+    // row panel.
     const int64_t band = t / (total_m * kBand);
     const int64_t within = t - band * total_m * kBand;
     const int64_t width = min((int64_t)kBand, ntj - band * kBand);
@@ -191,15 +200,7 @@ __device__ __forceinline__ TileDesc decode_tile(const GemmArgs& a, int* s_offs, 
     const int64_t nti = (a.I + kBM - 1) / kBM;
     const int64_t per_e = nti * ntj;
     const int64_t total = per_e * a.E;
-    // A tile's work grows with its expert's token count, so whole experts
-    // per XCD would leave the XCD holding the largest group of a skewed
-    // routing with most of the work.  Chunks of kWgChunk consecutive tiles
-    // (a band row: the same X rows, consecutive Y rows) are dealt round-robin
-    // over the 8 XCDs instead; workgroup b runs on XCD b % 8, and that XCD's
-    // i-th workgroup takes tile i % kWgChunk of its (i / kWgChunk)-th chunk.
-    const int64_t b = blockIdx.x;
-    const int64_t i = b >> 3;
-    const int64_t t = ((i / kWgChunk) * 8 + (b & 7)) * kWgChunk + i % kWgChunk;
+    const int64_t t = tile_of_workgroup(blockIdx.x);
     if (t >= total) return d;
     const int e = (int)(t / per_e);
     const int64_t r = t - e * per_e;
@@ -636,10 +637,9 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t st) {
   } else {
     tiles = (a.I + kBM - 1) / kBM * ntj * a.E;
   }
-  // mode 1 deals chunks of kWgChunk tiles round-robin over the 8 XCDs: every
-  // XCD gets as many workgroups as the XCD with the most chunks needs
-  const int64_t grid = a.mode == 0 ? (tiles + 7) / 8 * 8
-                                   : ((tiles + kWgChunk - 1) / kWgChunk + 7) / 8 * 8 * kWgChunk;
+  // chunks of kXcdChunk tiles go round-robin to the 8 XCDs (tile_of_workgroup):
+  // every XCD gets as many workgroups as the XCD with the most chunks needs
+  const int64_t grid = ((tiles + kXcdChunk - 1) / kXcdChunk + 7) / 8 * 8 * kXcdChunk;
   if (tiles == 0) return hipSuccess;
   const size_t lds = gemm_lds_bytes();
   const void* fn;
