@@ -2,23 +2,32 @@
 
 TEST INFRASTRUCTURE ONLY (tests, smoke check and bench's CPU leg).
 
-Criterion R1.  The target tolerance is a maximum relative error of 2e-3 for
-GEMM outputs accumulated in fp32.  The outputs are bf16, whose unit roundoff
-(2^-8) already exceeds 2e-3, and relative error is unbounded for outputs near
-zero.  R1 therefore charges the unavoidable half-ulp of the final bf16 rounding
-to the epilogue and applies 2e-3 to the rest, floored at sigma/16:
+The target is "max relative error 2e-3 (fp32 accumulation)" for GEMM
+outputs.  The outputs are bf16: their unit roundoff (2^-8) already exceeds
+2e-3, correctly rounded normal data has a normwise relative error of 1.66e-3,
+and relative error is unbounded for outputs near zero.  Three conditions,
+all required:
 
-    |g - r| <= 0.5 * ulp_bf16(max(|g|, |r|)) + 2e-3 * max(|r|, sigma / 16)
-               + U_MFMA * sum_k |x_k * y_k|
+(a) Elementwise bound (R1 plus the accumulation term):
 
-with g the result, r the fp64 oracle value and sigma the RMS of r over the
-output.  The last term is the classical dot-product error bound (unit
-roundoff times the sum of the absolute products).  The block-scaled MFMA of
-the target GPU does not sum its products exactly in fp32: measured against
-exact sums, a single instruction deviates by up to 2^-13.2 of its largest
-product, and whole GEMMs by up to 2.1e-4 (K=384) and 3.3e-5 (K=5120) of
-sum_k |x_k y_k|.  U_MFMA = 2^-11 keeps a margin of more than 2x over the
-worst case seen.  Pass abs_terms=None to apply R1 without that term.
+        |g - r| <= 0.5 * ulp_bf16(max(|g|, |r|)) + 2e-3 * max(|r|, sigma / 16)
+                   + U_MFMA * sum_k |x_k * y_k|
+
+    g is the result, r the fp64 oracle value, sigma the RMS of r over the
+    checked outputs.  The first term is the final bf16 rounding, the second
+    the 2e-3 relative bound floored at sigma/16, the third the classical
+    dot-product error bound (an error per unit of sum_k |x_k y_k|): the
+    block-scaled MFMA does not add its products exactly in fp32.  U_MFMA is
+    fixed from measurements of the hardware's summation error (below).
+
+(b) At most PLAIN_FRAC_MAX of the checked elements may need the third term:
+    everywhere else the plain R1 bound (first two terms) holds.  Elements
+    that need it are those whose sum nearly cancels (rows holding x50
+    outliers), where sum_k |x_k y_k| is far above |r| and sigma.
+
+(c) The normwise relative error ||g - r|| / ||r|| is at most 2e-3.
+
+f32=True compares unrounded fp32 results (no half-ulp term).
 """
 
 from __future__ import annotations
@@ -26,6 +35,20 @@ from __future__ import annotations
 import numpy as np
 
 REL_TOL = 2e-3
+NORMWISE_MAX = 2e-3
+PLAIN_FRAC_MAX = 2e-3
+
+
+# Accumulation-error coefficient of the block-scaled MFMA, per unit of
+# sum_k |x_k y_k|.  Measured maxima of |c - r| / sum_k |x_k y_k| for fp32
+# results c of whole GEMMs against exact sums r, K = 128 ... 8192 (seeded):
+# workload-like operands (N(0,1) with x50 outliers against N(0,0.02)) 2.0e-4
+# at K = 128 falling to 1.7e-5 at K = 8192; random codes with scales spread
+# over 30 binades 3.3e-4 at K = 128 and still 1.5e-4 at K = 8192, because a
+# few products dominate the sum there and the error does not average out
+# with K.  2^-11 = 4.9e-4 covers every measured case; it is applied only
+# through condition (a), while (b) and (c) bound how often and how much in
+# aggregate the plain R1 bound may be exceeded.
 U_MFMA = 2.0 ** -11
 
 
@@ -55,10 +78,11 @@ def rne_bf16(r: np.ndarray) -> np.ndarray:
 
 def r1_check(g_bits: np.ndarray, r: np.ndarray, sigma: float | None = None,
              abs_terms: np.ndarray | None = None, f32: bool = False) -> dict:
-    """Return a report dict; ``ok`` is True iff every element satisfies R1.
+    """Return a report dict; ``ok`` is True iff (a), (b) and (c) above hold.
 
     g_bits: bf16 bit patterns (or fp32 values with f32=True, no half-ulp term);
-    abs_terms: sum_k |x_k y_k| per element (same shape as r), or None.
+    abs_terms: sum_k |x_k y_k| per element (same shape as r), or None (then
+    condition (a) is the plain R1 bound).
     """
     g = np.asarray(g_bits, dtype=np.float64) if f32 else bf16_bits_to_f64(g_bits)
     r = np.asarray(r, dtype=np.float64)
@@ -74,17 +98,21 @@ def r1_check(g_bits: np.ndarray, r: np.ndarray, sigma: float | None = None,
         tol = tol + U_MFMA * np.asarray(abs_terms, dtype=np.float64)
     bad = ~(err <= tol)
     nrm = float(np.linalg.norm(r))
+    normwise = float(np.linalg.norm(g - r) / nrm) if nrm > 0 else float(np.linalg.norm(g))
+    plain_frac = float(plain_bad.mean()) if r.size else 0.0
     rep = {
-        "ok": not bool(bad.any()),
+        "ok_elementwise": not bool(bad.any()),
         "n": int(r.size),
         "n_bad": int(bad.sum()),
         "max_err_over_tol": float(np.max(err / np.maximum(tol, 1e-300))) if r.size else 0.0,
-        "normwise_rel": float(np.linalg.norm(g - r) / nrm) if nrm > 0 else float(np.linalg.norm(g)),
+        "normwise_rel": normwise,
         "exact_rne_rate": float(np.mean(g == rne_bf16(r))) if r.size else 1.0,
         "plain_r1_violations": int(plain_bad.sum()),
+        "plain_r1_frac": plain_frac,
         "max_err_over_abs_terms": float(np.max(err / np.maximum(abs_terms, 1e-300))) if abs_terms is not None and r.size else None,
         "sigma": sigma,
     }
+    rep["ok"] = rep["ok_elementwise"] and plain_frac <= PLAIN_FRAC_MAX and normwise <= NORMWISE_MAX
     if bad.any():
         idx = np.argwhere(bad)[:5]
         rep["first_bad"] = [(tuple(int(v) for v in i), float(g[tuple(i)]), float(r[tuple(i)])) for i in idx]

@@ -270,7 +270,10 @@ def _pow2_tensor(shape, seed):
 
 def test_adjoint_identity_fwd_dgrad_wgrad():
     """With lossless operands <dOut, fwd(A,W)> = <dA, A> = <dW, W> exactly;
-    a transposed operand, a wrong group or a wrong block axis breaks it."""
+    a transposed operand or a wrong group breaks it.  The +-2^j operands
+    quantize losslessly along any axis, so this test cannot see which axis an
+    operand is blocked along: test_block_axis_hand_case and the exact-rational
+    brute forces pin that."""
     counts = [32, 0, 64, 32]
     offs = inp.offsets_from_counts(counts)
     M, K, N, E = 128, 96, 64, 4
@@ -341,3 +344,189 @@ def test_absolute_companion_bounds_the_sum():
         assert (absd >= np.abs(plain) - 1e-12 * absd).all()
         pos = (a & 0x7FFF, b & 0x7FFF)                          # clear sign bits
         np.testing.assert_allclose(fn(*pos, offs, absolute=True), fn(*pos, offs), rtol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Block axis of each GEMM operand (hand-worked, tests/golden/block_axis_hand.json)
+# --------------------------------------------------------------------------
+def _dyadic(expr: str, c: Fraction) -> Fraction:
+    """Exact value of a sum of products of integers, 'c' and 'b^e' terms."""
+    total = Fraction(0)
+    for term in expr.split("+"):
+        val = Fraction(1)
+        for f in term.strip().split("*"):
+            f = f.strip()
+            if f == "c":
+                val *= c
+            elif "^" in f:
+                b, e = f.split("^")
+                val *= Fraction(int(b)) ** int(e)
+            else:
+                val *= Fraction(int(f))
+        total += val
+    return total
+
+
+def _block_axis_cases():
+    with open(os.path.join(GOLDEN, "block_axis_hand.json")) as f:
+        doc = json.load(f)
+    c = _dyadic(doc["c"], Fraction(0))
+    return [(case, c) for case in doc["cases"]]
+
+
+@pytest.mark.parametrize("case,c", _block_axis_cases(), ids=lambda v: v["id"] if isinstance(v, dict) else "")
+def test_block_axis_hand_case(case, c):
+    """fwd blocks W along K, dgrad along N, wgrad blocks both operands along
+    the tokens: exact results derived by hand, told apart from the other axis."""
+    cf = float(c)
+    one = np.ones
+    ex = {k: _dyadic(v, c) for k, v in case["expect"].items()}
+    wr = {k: _dyadic(v, c) for k, v in case["wrong"].items()}
+    assert all(ex[k] != wr[k] for k in ex)
+    if case["op"] in ("fwd", "dgrad"):
+        W = np.full((1, 32, 32), cf)
+        W[0, 0, 1] = 1024.0
+        Wb = _bf16_exact(W.astype(np.float32))
+        X = _bf16_exact(one((1, 32), np.float32))
+        offs = np.array([1], dtype=np.int32)
+        if case["op"] == "fwd":
+            out = oracle.grouped_mm_fwd(X, Wb, offs)
+            assert Fraction(float(out[0, 0])) == ex["out[0,0]"]
+            assert all(Fraction(float(v)) == ex["out[0,n>=1]"] for v in out[0, 1:])
+        else:
+            out = oracle.grouped_mm_dgrad(X, Wb, offs)
+            assert Fraction(float(out[0, 1])) == ex["dA[0,1]"]
+            assert all(Fraction(float(v)) == ex["dA[0,k!=1]"] for k, v in enumerate(out[0]) if k != 1)
+    else:
+        A = np.full((32, 32), cf)
+        A[0, 0] = 1024.0
+        Ab = _bf16_exact(A.astype(np.float32))
+        G = _bf16_exact(one((32, 1), np.float32))
+        out = oracle.grouped_mm_wgrad(G, Ab, np.array([32], dtype=np.int32))
+        assert out.shape == (1, 1, 32)
+        assert Fraction(float(out[0, 0, 0])) == ex["dW[0,0,0]"]
+        assert all(Fraction(float(v)) == ex["dW[0,0,k>=1]"] for v in out[0, 0, 1:])
+
+
+def test_grouped_dgrad_exact_rational_bruteforce():
+    """Independent route for dgrad: W[e] blocked along N equals the rowwise
+    quantization of W[e]^T [K, N]; inputs are not lossless and every 32-row
+    block of N has its own magnitude, so blocking along K would differ."""
+    counts = [4, 0, 6]
+    offs = inp.offsets_from_counts(counts)
+    M, N, K, E = sum(counts), 64, 32, 3
+    G = inp.random_bf16((M, N), seed=25, std=1e-3, outliers=True)
+    rng = np.random.default_rng(26)
+    Wf = rng.standard_normal((E, N, K)).astype(np.float32) * np.float32(0.02)
+    Wf *= np.repeat(np.float32(2.0) ** rng.integers(-6, 7, size=(E, N // 32, K)).astype(np.float32), 32, axis=1)
+    Wf[rng.random((E, N, K)) < 0.02] *= np.float32(60.0)
+    W = inp.f32_to_bf16_bits(Wf)
+    got = oracle.grouped_mm_dgrad(G, W, offs)
+    qG, sG = oracle.quantize_rowwise(G)
+    dG = oracle.dequant_rowwise(qG, sG)
+    start = 0
+    for e, c in enumerate(counts):
+        qWt, sWt = oracle.quantize_rowwise(np.ascontiguousarray(W[e].T))      # [K, N], blocks along N
+        exact = _exact_dot_rows(dG[start:start + c], oracle.dequant_rowwise(qWt, sWt))
+        for i in range(c):
+            for k in range(K):
+                r = float(exact[i][k])
+                assert abs(got[start + i, k] - r) <= 1e-14 * max(1e-9, abs(r))
+        start += c
+    # the K-blocked reading gives a different result on these inputs
+    qW, sW = oracle.quantize_rowwise(W[2])
+    wrong = dG[4:10] @ oracle.dequant_rowwise(qW, sW)
+    assert not np.allclose(wrong, got[4:10], rtol=1e-6, atol=0)
+
+
+# --------------------------------------------------------------------------
+# 32x32 element placement and its dequantization
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("blk", _hand_blocks(), ids=lambda b: b["id"])
+@pytest.mark.parametrize("where", ["row", "col"])
+def test_32x32_hand_block_in_zero_tile(blk, where):
+    """A hand-worked block placed as row 5 (or column 9) of an otherwise +0
+    tile: the tile's amax is the block's, so the scale and the codes at those
+    positions are the hand-derived ones and every other code is 0x00 (a NaN or
+    Inf makes the whole tile 0x7F)."""
+    vals = [_parse_value(s) for s in blk["values"]]
+    vals += [_parse_value(blk["fill"])] * (32 - len(vals))
+    codes = [int(c, 16) for c in blk["codes"]]
+    codes += [int(blk["fill_code"], 16)] * (32 - len(codes))
+    tile = np.zeros((32, 32), dtype=np.float32)
+    if where == "row":
+        tile[5, :] = vals
+    else:
+        tile[:, 9] = vals
+    q, s = oracle.quantize_32x32(_bf16_exact(tile))
+    assert s.shape == (1, 1) and int(s[0, 0]) == int(blk["scale"], 16)
+    if int(blk["scale"], 16) == 0xFF:
+        assert (q == 0x7F).all()
+        return
+    want = np.zeros((32, 32), dtype=np.uint8)
+    if where == "row":
+        want[5, :] = codes
+    else:
+        want[:, 9] = codes
+    np.testing.assert_array_equal(q, want)
+
+
+def test_32x32_codes_equal_rowwise_when_rows_share_the_tile_amax():
+    """If every row of a tile holds the tile's largest magnitude, each row's
+    1x32 scale is the tile's scale, so the 32x32 codes must equal the rowwise
+    codes element for element (an in-tile transpose would not)."""
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((2, 64, 96)).astype(np.float32)
+    x[rng.random(x.shape) < 0.01] *= np.float32(30.0)
+    xb = inp.bf16_bits_to_f32(inp.f32_to_bf16_bits(x))
+    for b in range(2):
+        for tr in range(2):
+            for tc in range(3):
+                t = xb[b, 32 * tr:32 * tr + 32, 32 * tc:32 * tc + 32]
+                amax = np.abs(t).max()
+                cols = rng.integers(0, 32, size=32)
+                t[np.arange(32), cols] = amax * rng.choice([-1.0, 1.0], size=32)
+    bits = inp.f32_to_bf16_bits(xb)
+    q32, s32 = oracle.quantize_32x32(bits)
+    qr, sr = oracle.quantize_rowwise(bits)
+    np.testing.assert_array_equal(q32, qr)
+    np.testing.assert_array_equal(np.repeat(s32, 32, axis=1), sr)
+    assert len(np.unique(s32)) > 1
+
+
+def test_dequant_32x32_closed_form_and_round_trip():
+    """Closed form: code 0x38 (1.0) everywhere with a distinct scale byte per
+    tile dequantizes to 2^(byte-127) over exactly that tile.  Round trip:
+    values +-2^j within 17 binades of their tile's largest come back exactly."""
+    s = np.array([[120, 121, 122], [123, 124, 125]], dtype=np.uint8)
+    q = np.full((64, 96), 0x38, dtype=np.uint8)
+    d = oracle.dequant_32x32(q, s)
+    for i in range(2):
+        for j in range(3):
+            assert (d[32 * i:32 * i + 32, 32 * j:32 * j + 32] == 2.0 ** (int(s[i, j]) - 127)).all()
+    rng = np.random.default_rng(16)
+    top = rng.integers(-20, 20, size=(1, 2, 3))
+    j = np.repeat(np.repeat(top, 32, axis=1), 32, axis=2) - rng.integers(0, 18, size=(1, 64, 96))
+    v = (rng.choice([-1.0, 1.0], size=j.shape) * np.exp2(j.astype(np.float64))).astype(np.float32)
+    bits = _bf16_exact(v)
+    q3, s3 = oracle.quantize_32x32(bits)
+    np.testing.assert_array_equal(oracle.dequant_32x32(q3, s3), oracle.bf16_to_f64(bits))
+
+
+def test_r1_rejects_widespread_small_regressions():
+    """An error of 1% of sigma on every element stays inside the elementwise
+    bound wherever sum_k |x_k y_k| is large, but fails the normwise bound;
+    an error of 0.02 sigma on 1% of the elements fails the plain-R1 fraction."""
+    rng = np.random.default_rng(6)
+    r = rng.standard_normal((64, 512))
+    absd = np.full(r.shape, 60.0)           # sum_k |x_k y_k| of a K ~ 5000 product
+    ok = inp.f32_to_bf16_bits(oracle.rne_bf16(r).astype(np.float32))
+    assert oracle.r1_check(ok, r, abs_terms=absd)["ok"]
+    noisy = r + 0.01 * rng.choice([-1.0, 1.0], size=r.shape)
+    rep = oracle.r1_check(inp.f32_to_bf16_bits(noisy.astype(np.float32)), r, abs_terms=absd)
+    assert rep["ok_elementwise"] and rep["normwise_rel"] > 2e-3 and not rep["ok"]
+    few = r.copy()
+    idx = rng.random(r.shape) < 0.01
+    few[idx] += 0.02 * np.sign(r[idx])
+    rep = oracle.r1_check(inp.f32_to_bf16_bits(few.astype(np.float32)), r, abs_terms=absd)
+    assert rep["ok_elementwise"] and rep["plain_r1_frac"] > 2e-3 and not rep["ok"]
