@@ -52,9 +52,12 @@
  *     launched; mx_last_error() then describes it (thread-local text).
  *   - Group offsets live on the device and are not checked against the host.
  *     Preconditions: non-decreasing, offs[E-1] == M, and for wgrad every
- *     group start a multiple of 32.  Kernels clamp offsets into [0, M], so a
- *     violation never reads or writes out of bounds; the values are then
- *     unspecified.
+ *     group start a multiple of 32.  mx_check_offsets tests them on the
+ *     device.  Kernels clamp offsets into the operand's extent (the rows of
+ *     X in mode 0; the contraction length Kc in mode 1, which the wgrad
+ *     entry point pads with zero codes from M up to M rounded to 128) and
+ *     round wgrad group bounds down to multiples of 32, so a violation never
+ *     reads or writes out of bounds; the values are then unspecified.
  *   - No global state besides the error text: calls are reentrant.
  */
 #ifndef MXMOE_H
@@ -73,8 +76,18 @@ typedef enum mx_status {
   MX_ERR_SHAPE = 2,      /* a size is negative or violates a divisibility rule */
   MX_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned                   */
   MX_ERR_WORKSPACE = 4,  /* workspace smaller than mx_grouped_mm_workspace_bytes */
-  MX_ERR_HIP = 5         /* a kernel launch failed (text has the HIP error)    */
+  MX_ERR_HIP = 5,        /* a kernel launch failed (text has the HIP error)    */
+  MX_ERR_LAYOUT = 6      /* scales passed in a layout the callee does not read */
 } mx_status;
+
+/* Arrangement of E8M0 scale bytes.  The quantizers write row-major scales
+ * [rows][K/32]; the GEMM reads its blocked layout [K/128][rows][4] (see
+ * mx_scales_to_gemm_layout).  The GEMM entry points take the layout of the
+ * scales they are given and refuse anything but MX_SCALES_GEMM. */
+typedef enum mx_scale_layout {
+  MX_SCALES_ROWMAJOR = 0,
+  MX_SCALES_GEMM = 1
+} mx_scale_layout;
 
 /* Text describing the last non-OK status returned on this thread. */
 const char* mx_last_error(void);
@@ -131,7 +144,8 @@ mx_status mx_scales_to_gemm_layout(const uint8_t* s, int64_t batch, int64_t rows
  *           C[e] = 0.  Group starts must be multiples of 32.
  * Scale tensors are passed in the GEMM layout of mx_scales_to_gemm_layout
  * (sX with batch 1 and rows I; sY with batch E and rows J in mode 0, batch 1
- * and rows J in mode 1).
+ * and rows J in mode 1), and scale_layout must say so (MX_SCALES_GEMM);
+ * MX_SCALES_ROWMAJOR returns MX_ERR_LAYOUT.
  * offs: int32 [E] cumulative END offsets on the device (offs[-1] = 0),
  * over rows of X (mode 0) or over k (mode 1).
  * Requires Kc % 128 == 0, J % 8 == 0, E >= 1.
@@ -140,15 +154,35 @@ mx_status mx_scales_to_gemm_layout(const uint8_t* s, int64_t batch, int64_t rows
  * wgrad X = q_t(dOut) [N, M], Y = q_t(A) [K, M] (colwise along tokens).
  * ------------------------------------------------------------------------ */
 mx_status mx_grouped_gemm_mx(const uint8_t* X, const uint8_t* sX, const uint8_t* Y, const uint8_t* sY,
-                             const int32_t* offs, int mode, int64_t I, int64_t J, int64_t Kc, int64_t E,
-                             uint16_t* C, void* stream);
+                             int scale_layout, const int32_t* offs, int mode, int64_t I, int64_t J, int64_t Kc,
+                             int64_t E, uint16_t* C, void* stream);
 
 /* The same GEMM with the fp32 accumulators stored unrounded (C is float,
  * same shapes and rules).  For callers that accumulate results in fp32, e.g.
  * weight gradients summed over micro-batches before the optimizer step. */
 mx_status mx_grouped_gemm_mx_f32(const uint8_t* X, const uint8_t* sX, const uint8_t* Y, const uint8_t* sY,
-                                 const int32_t* offs, int mode, int64_t I, int64_t J, int64_t Kc, int64_t E,
-                                 float* C, void* stream);
+                                 int scale_layout, const int32_t* offs, int mode, int64_t I, int64_t J, int64_t Kc,
+                                 int64_t E, float* C, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Validity of group offsets, tested on the device (no host round trip; the
+ * caller reads *status when it chooses to).  offs: int32 [E] cumulative END
+ * offsets on the device; status: one int32 on the device, set to 0 when
+ * every offset is valid, else to the OR of
+ *   MX_OFFS_DECREASING  an offset below its predecessor (offs[-1] = 0),
+ *   MX_OFFS_RANGE       an offset outside [0, M],
+ *   MX_OFFS_LAST        offs[E-1] != M,
+ *   MX_OFFS_ALIGN       a group start that is not a multiple of `align`
+ *                       (the weight gradient needs align = 32: its 32-token
+ *                       blocks must not straddle two experts).
+ * Unsupported inputs get a clear error before they reach a GEMM ("feat(moe):
+ * add MoK MXFP8 expert support" PR, summary).
+ * ------------------------------------------------------------------------ */
+#define MX_OFFS_DECREASING 1
+#define MX_OFFS_RANGE 2
+#define MX_OFFS_LAST 4
+#define MX_OFFS_ALIGN 8
+mx_status mx_check_offsets(const int32_t* offs, int64_t E, int64_t M, int32_t align, int32_t* status, void* stream);
 
 /* ------------------------------------------------------------------------
  * The grouped GEMMs on bf16 inputs: quantize both operands into the caller's

@@ -21,12 +21,15 @@ __all__ = [
     "mx_grouped_mm_fwd", "mx_grouped_mm_dgrad", "mx_grouped_mm_wgrad",
     "mx_quantize_weights", "mx_quantize_dual", "mx_quantize_rowwise_gather",
     "mx_grouped_mm_fwd_q", "mx_grouped_mm_dgrad_q", "mx_grouped_mm", "mx_linear",
-    "OP_FWD", "OP_DGRAD", "OP_WGRAD", "OP_FWD_Q", "OP_DGRAD_Q",
+    "OP_FWD", "OP_DGRAD", "OP_WGRAD", "OP_FWD_Q", "OP_DGRAD_Q", "SCALES_ROWMAJOR", "SCALES_GEMM",
+    "mx_check_offsets", "check_offsets",
 ]
 
 OP_FWD, OP_DGRAD, OP_WGRAD, OP_FWD_Q, OP_DGRAD_Q = 0, 1, 2, 3, 4
+SCALES_ROWMAJOR, SCALES_GEMM = 0, 1
+OFFS_DECREASING, OFFS_RANGE, OFFS_LAST, OFFS_ALIGN = 1, 2, 4, 8
 _STATUS = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN", 4: "MX_ERR_WORKSPACE",
-           5: "MX_ERR_HIP"}
+           5: "MX_ERR_HIP", 6: "MX_ERR_LAYOUT"}
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -63,7 +66,9 @@ def load_library():
     for name in ("mx_grouped_gemm_mx", "mx_grouped_gemm_mx_f32"):
         f = getattr(lib, name)
         f.restype = c_int
-        f.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp]
+        f.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, c_vp, c_int, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp]
+    lib.mx_check_offsets.restype = c_int
+    lib.mx_check_offsets.argtypes = [c_vp, c_i64, c_i64, ctypes.c_int32, c_vp, c_vp]
     lib.mx_scales_to_gemm_layout.restype = c_int
     lib.mx_scales_to_gemm_layout.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]
     lib.mx_grouped_mm_workspace_bytes.restype = c_sz
@@ -198,17 +203,22 @@ def mx_scales_to_gemm_layout(s, out=None):
 # ---------------------------------------------------------------------------
 # Grouped GEMM on prequantized operands
 # ---------------------------------------------------------------------------
-def mx_grouped_gemm_mx(X, sX, Y, sY, offs, mode: int, out=None, out_dtype=None):
+def mx_grouped_gemm_mx(X, sX, Y, sY, offs, mode: int, out=None, out_dtype=None, scale_layout: str = "gemm"):
     """C[i,j] = sum_k X[i,k] Y[j,k] 2^(sX+sY-254).  mode 0: Y [E,J,Kc], C [I,J];
-    mode 1 (groups over k): Y [J,Kc], C [E,I,J].  Scales sX, sY are in the
-    GEMM layout (mx_scales_to_gemm_layout).  Returns C (bf16, or fp32 with
-    out_dtype=torch.float32)."""
+    mode 1 (groups over k): Y [J,Kc], C [E,I,J].  The scales must be in the
+    GEMM's blocked layout (what mx_quantize_weights / mx_quantize_dual write,
+    or mx_scales_to_gemm_layout of a quantizer's row-major scales):
+    sX [Kc/128, I, 4]; sY [E, Kc/128, J, 4] in mode 0, [Kc/128, J, 4] in mode 1.
+    Row-major scales raise (their shapes differ).  Returns C (bf16, or fp32
+    with out_dtype=torch.float32)."""
     import torch
     lib = load_library()
     if out_dtype is None:
         out_dtype = out.dtype if out is not None else torch.bfloat16
     if out_dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    if scale_layout not in ("gemm", "rowmajor"):
+        raise ValueError("scale_layout must be 'gemm' or 'rowmajor'")
     for t, n in ((X, "X"), (sX, "sX"), (Y, "Y"), (sY, "sY")):
         _require(t, torch.uint8, n)
     _require(offs, torch.int32, "offs")
@@ -220,20 +230,22 @@ def mx_grouped_gemm_mx(X, sX, Y, sY, offs, mode: int, out=None, out_dtype=None):
         if Y.dim() != 3 or Y.shape[0] != E or Y.shape[2] != Kc:
             raise ValueError(f"mode 0: Y must be [E={E}, J, Kc={Kc}], got {tuple(Y.shape)}")
         J = Y.shape[1]
-        y_rows = E * J
     else:
         if Y.dim() != 2 or Y.shape[1] != Kc:
             raise ValueError(f"mode 1: Y must be [J, Kc={Kc}], got {tuple(Y.shape)}")
         J = Y.shape[0]
-        y_rows = J
-    # scales hold one byte per 32 contraction bytes of every operand row (any
-    # arrangement of that size: row-major or the GEMM layout)
-    if sX.numel() != I * (Kc // 32) or sY.numel() != y_rows * (Kc // 32):
-        raise ValueError(f"sX / sY must hold {I * (Kc // 32)} / {y_rows * (Kc // 32)} bytes, "
-                         f"got {sX.numel()} / {sY.numel()}")
+    if scale_layout == "gemm":
+        want_x = (Kc // 128, I, 4)
+        want_y = (E, Kc // 128, J, 4) if mode == 0 else (Kc // 128, J, 4)
+        for t, want, n in ((sX, want_x, "sX"), (sY, want_y, "sY")):
+            if tuple(t.shape) != want:
+                hint = (" (these are row-major scales: convert them with mx_scales_to_gemm_layout)"
+                        if t.dim() == len(want) - 1 and t.shape[-1] == Kc // 32 else "")
+                raise ValueError(f"{n} must be in the GEMM scale layout {want}, got {tuple(t.shape)}{hint}")
     out = _out(out, (I, J) if mode == 0 else (E, I, J), out_dtype, X.device, "out")
     name = "mx_grouped_gemm_mx" if out_dtype == torch.bfloat16 else "mx_grouped_gemm_mx_f32"
-    _check(name, getattr(lib, name)(_ptr(X), _ptr(sX), _ptr(Y), _ptr(sY), _ptr(offs), mode, I, J, Kc, E,
+    layout = SCALES_GEMM if scale_layout == "gemm" else SCALES_ROWMAJOR
+    _check(name, getattr(lib, name)(_ptr(X), _ptr(sX), _ptr(Y), _ptr(sY), layout, _ptr(offs), mode, I, J, Kc, E,
                                     _ptr(out), _stream(X.device)))
     return out
 
@@ -419,10 +431,38 @@ def mx_grouped_mm_dgrad_q(dOut, qWt, sWt, offs, out=None, ws=None):
     return out
 
 
-def mx_grouped_mm(A, W, offs):
+def mx_check_offsets(offs, M: int, align: int = 1, status=None):
+    """Validity bitmask of the group offsets, computed on the device into
+    `status` (int32 [1] on the GPU; returned without synchronizing).  0 = valid;
+    OFFS_DECREASING / OFFS_RANGE / OFFS_LAST / OFFS_ALIGN otherwise."""
+    import torch
+    lib = load_library()
+    _require(offs, torch.int32, "offs")
+    if offs.dim() != 1:
+        raise ValueError("offs must be int32 [E]")
+    status = _out(status, (1,), torch.int32, offs.device, "status")
+    _check("mx_check_offsets", lib.mx_check_offsets(_ptr(offs), offs.shape[0], int(M), int(align), _ptr(status),
+                                                    _stream(offs.device)))
+    return status
+
+
+def check_offsets(offs, M: int, align: int = 1):
+    """Raise ValueError, naming every violated rule, unless the group offsets
+    are valid (reads the device status word: one synchronization)."""
+    bits = int(mx_check_offsets(offs, M, align).item())
+    if bits:
+        why = [text for bit, text in ((OFFS_DECREASING, "an offset is below its predecessor"),
+                                      (OFFS_RANGE, f"an offset lies outside [0, {M}]"),
+                                      (OFFS_LAST, f"the last offset is not M={M}"),
+                                      (OFFS_ALIGN, f"a group starts off a multiple of {align} (pad every group "
+                                                   f"with zero rows to a multiple of {align})")) if bits & bit]
+        raise ValueError("invalid group offsets: " + "; ".join(why))
+
+
+def mx_grouped_mm(A, W, offs, check_offsets: bool = True):
     """Differentiable MXFP8 grouped GEMM (forward, dgrad, wgrad in the library's kernels)."""
     from .autograd import mx_grouped_mm as _f
-    return _f(A, W, offs)
+    return _f(A, W, offs, check_offsets)
 
 
 def mx_linear(x, weight):

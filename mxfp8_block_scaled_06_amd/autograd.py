@@ -15,7 +15,9 @@ the backward quantizes dOut in both orientations (dgrad and wgrad) from one
 read.  Every step runs in the library's kernels; this module only wires them
 into torch.autograd.
 
-Contract (checked here, with a clear error otherwise):
+Contract (checked here, with a clear error otherwise; the group offsets are
+checked on the device, one synchronization per call, unless
+check_offsets=False):
   A    bf16 [M, K] tokens grouped by expert (offs: int32 [E] END offsets on
        the device), every group start a multiple of 32 (pad groups with zero
        rows) and M % 32 == 0 -- the weight gradient sums 32-token blocks that
@@ -30,7 +32,7 @@ from . import (mx_grouped_gemm_mx, mx_grouped_mm_dgrad_q, mx_grouped_mm_fwd_q, m
                mx_quantize_weights)
 
 
-def _check(A, W, offs):
+def _check(A, W, offs, check_offsets=True):
     import torch
     if A.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
         raise TypeError("mx_grouped_mm: A and W must be bfloat16")
@@ -48,6 +50,10 @@ def _check(A, W, offs):
         raise ValueError(f"mx_grouped_mm: N={N} and K={K} must be multiples of 128")
     if M % 32:
         raise ValueError(f"mx_grouped_mm: M={M} must be a multiple of 32 (pad every group to 32 rows)")
+    if check_offsets and A.is_cuda:
+        # the weight gradient's 32-token blocks must not straddle two experts
+        from . import check_offsets as _chk
+        _chk(offs, M, 32)
 
 
 class _MXGroupedMM:
@@ -98,9 +104,9 @@ class _MXGroupedMM:
         return cls.fn
 
 
-def mx_grouped_mm(A, W, offs):
+def mx_grouped_mm(A, W, offs, check_offsets: bool = True):
     """Differentiable out[g_e] = A[g_e] @ W[e]^T with MXFP8 operands (see the module docstring)."""
-    _check(A, W, offs)
+    _check(A, W, offs, check_offsets)
     return _MXGroupedMM.get().apply(A.contiguous(), W.contiguous(), offs)
 
 

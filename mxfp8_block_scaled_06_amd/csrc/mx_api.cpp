@@ -161,8 +161,17 @@ mx_status mx_quantize_32x32(const uint16_t* x, int64_t batch, int64_t rows, int6
 namespace {
 
 mx_status grouped_gemm_impl(const char* fn, const uint8_t* X, const uint8_t* sX, const uint8_t* Y,
-                            const uint8_t* sY, const int32_t* offs, int mode, int64_t I, int64_t J, int64_t Kc,
-                            int64_t E, void* C, int out_f32, void* stream) {
+                            const uint8_t* sY, int scale_layout, const int32_t* offs, int mode, int64_t I, int64_t J,
+                            int64_t Kc, int64_t E, void* C, int out_f32, void* stream) {
+  if (scale_layout == MX_SCALES_ROWMAJOR)
+    return fail(MX_ERR_LAYOUT,
+                "%s: the GEMM reads scales in its blocked layout [K/128][rows][4]; row-major scales "
+                "[rows][K/32] (what mx_quantize_rowwise / mx_quantize_colwise write) must be converted with "
+                "mx_scales_to_gemm_layout first (mx_quantize_weights and mx_quantize_dual write the GEMM layout)",
+                fn);
+  if (scale_layout != MX_SCALES_GEMM)
+    return fail(MX_ERR_LAYOUT, "%s: unknown scale layout %d (MX_SCALES_GEMM = %d)", fn, scale_layout,
+                (int)MX_SCALES_GEMM);
   if (mode != 0 && mode != 1) return fail(MX_ERR_SHAPE, "%s: mode must be 0 or 1 (got %d)", fn, mode);
   if (I < 0 || J < 0 || Kc < 0) return fail(MX_ERR_SHAPE, "%s: negative size", fn);
   if (E < 1 || E > mxk::kMaxExperts)
@@ -207,15 +216,27 @@ mx_status grouped_gemm_impl(const char* fn, const uint8_t* X, const uint8_t* sX,
 extern "C" {
 
 mx_status mx_grouped_gemm_mx(const uint8_t* X, const uint8_t* sX, const uint8_t* Y, const uint8_t* sY,
-                             const int32_t* offs, int mode, int64_t I, int64_t J, int64_t Kc, int64_t E, uint16_t* C,
-                             void* stream) {
-  return grouped_gemm_impl("mx_grouped_gemm_mx", X, sX, Y, sY, offs, mode, I, J, Kc, E, C, 0, stream);
+                             int scale_layout, const int32_t* offs, int mode, int64_t I, int64_t J, int64_t Kc,
+                             int64_t E, uint16_t* C, void* stream) {
+  return grouped_gemm_impl("mx_grouped_gemm_mx", X, sX, Y, sY, scale_layout, offs, mode, I, J, Kc, E, C, 0, stream);
 }
 
 mx_status mx_grouped_gemm_mx_f32(const uint8_t* X, const uint8_t* sX, const uint8_t* Y, const uint8_t* sY,
-                                 const int32_t* offs, int mode, int64_t I, int64_t J, int64_t Kc, int64_t E, float* C,
-                                 void* stream) {
-  return grouped_gemm_impl("mx_grouped_gemm_mx_f32", X, sX, Y, sY, offs, mode, I, J, Kc, E, C, 1, stream);
+                                 int scale_layout, const int32_t* offs, int mode, int64_t I, int64_t J, int64_t Kc,
+                                 int64_t E, float* C, void* stream) {
+  return grouped_gemm_impl("mx_grouped_gemm_mx_f32", X, sX, Y, sY, scale_layout, offs, mode, I, J, Kc, E, C, 1,
+                           stream);
+}
+
+mx_status mx_check_offsets(const int32_t* offs, int64_t E, int64_t M, int32_t align, int32_t* status, void* stream) {
+  const char* fn = "mx_check_offsets";
+  if (E < 1 || E > mxk::kMaxExperts)
+    return fail(MX_ERR_SHAPE, "%s: number of experts E=%lld outside [1, %d]", fn, (long long)E, mxk::kMaxExperts);
+  if (M < 0 || M > INT32_MAX) return fail(MX_ERR_SHAPE, "%s: M=%lld outside [0, 2^31)", fn, (long long)M);
+  if (align < 1) return fail(MX_ERR_SHAPE, "%s: align=%d must be >= 1", fn, (int)align);
+  if (!offs || !status) return fail(MX_ERR_NULL, "%s: null pointer", fn);
+  if (!aligned(offs, 4) || !aligned(status, 4)) return fail(MX_ERR_ALIGN, "%s: offs and status must be 4-byte aligned", fn);
+  return hip_status(mxk::launch_check_offsets(offs, E, M, align, status, (hipStream_t)stream), fn);
 }
 
 mx_status mx_scales_to_gemm_layout(const uint8_t* s, int64_t batch, int64_t rows, int64_t kblocks, uint8_t* s_gemm,
@@ -254,7 +275,7 @@ mx_status mx_grouped_mm_fwd(const uint16_t* A, const uint16_t* W, const int32_t*
   uint8_t *qA = w8 + L.off[0], *sA = w8 + L.off[1], *qW = w8 + L.off[2], *sW = w8 + L.off[3];
   if ((st = hip_status(mxk::launch_quant_rowwise(A, M, K, qA, sA, M, s), "fwd quantize A")) != MX_OK) return st;
   if ((st = hip_status(mxk::launch_quant_rowwise(W, E * N, K, qW, sW, N, s), "fwd quantize W")) != MX_OK) return st;
-  return mx_grouped_gemm_mx(qA, sA, qW, sW, offs, 0, M, N, K, E, out, stream);
+  return mx_grouped_gemm_mx(qA, sA, qW, sW, MX_SCALES_GEMM, offs, 0, M, N, K, E, out, stream);
 }
 
 mx_status mx_grouped_mm_dgrad(const uint16_t* dOut, const uint16_t* W, const int32_t* offs, int64_t M, int64_t N,
@@ -279,7 +300,7 @@ mx_status mx_grouped_mm_dgrad(const uint16_t* dOut, const uint16_t* W, const int
   // W [E, N, K] quantized in 32-blocks along N, stored transposed [E, K, N]
   if ((st = hip_status(mxk::launch_quant_colwise(W, E, N, K, qWt, N, sWt, N / 32, 1, s), "dgrad quantize W")) != MX_OK)
     return st;
-  return mx_grouped_gemm_mx(qG, sG, qWt, sWt, offs, 0, M, K, N, E, dA, stream);
+  return mx_grouped_gemm_mx(qG, sG, qWt, sWt, MX_SCALES_GEMM, offs, 0, M, K, N, E, dA, stream);
 }
 
 mx_status mx_grouped_mm_wgrad(const uint16_t* dOut, const uint16_t* A, const int32_t* offs, int64_t M, int64_t N,
@@ -307,7 +328,7 @@ mx_status mx_grouped_mm_wgrad(const uint16_t* dOut, const uint16_t* A, const int
   if ((st = hip_status(mxk::launch_quant_colwise(A, 1, M, K, qAt, Mp, sAt, Mp / 32, 1, s), "wgrad quantize A")) !=
       MX_OK)
     return st;
-  return mx_grouped_gemm_mx(qGt, sGt, qAt, sAt, offs, 1, N, K, Mp, E, dW, stream);
+  return mx_grouped_gemm_mx(qGt, sGt, qAt, sAt, MX_SCALES_GEMM, offs, 1, N, K, Mp, E, dW, stream);
 }
 
 mx_status mx_quantize_weights(const uint16_t* w, int64_t E, int64_t N, int64_t K, uint8_t* q, uint8_t* s,
@@ -363,7 +384,7 @@ mx_status mx_grouped_mm_fwd_q(const uint16_t* A, const uint8_t* qW, const uint8_
   hipStream_t s = (hipStream_t)stream;
   uint8_t *qA = w8 + L.off[0], *sA = w8 + L.off[1];
   if ((st = hip_status(mxk::launch_quant_rowwise(A, M, K, qA, sA, M, s), "fwd_q quantize A")) != MX_OK) return st;
-  return mx_grouped_gemm_mx(qA, sA, qW, sW, offs, 0, M, N, K, E, out, stream);
+  return mx_grouped_gemm_mx(qA, sA, qW, sW, MX_SCALES_GEMM, offs, 0, M, N, K, E, out, stream);
 }
 
 mx_status mx_grouped_mm_dgrad_q(const uint16_t* dOut, const uint8_t* qWt, const uint8_t* sWt, const int32_t* offs,
@@ -386,7 +407,7 @@ mx_status mx_grouped_mm_dgrad_q(const uint16_t* dOut, const uint8_t* qWt, const 
   uint8_t *qG = w8 + L.off[0], *sG = w8 + L.off[1];
   if ((st = hip_status(mxk::launch_quant_rowwise(dOut, M, N, qG, sG, M, s), "dgrad_q quantize dOut")) != MX_OK)
     return st;
-  return mx_grouped_gemm_mx(qG, sG, qWt, sWt, offs, 0, M, K, N, E, dA, stream);
+  return mx_grouped_gemm_mx(qG, sG, qWt, sWt, MX_SCALES_GEMM, offs, 0, M, K, N, E, dA, stream);
 }
 
 mx_status mx_quantize_rowwise_gather(const uint16_t* x, int64_t src_rows, const int32_t* rows, int64_t M,

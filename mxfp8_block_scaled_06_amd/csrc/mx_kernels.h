@@ -47,6 +47,9 @@ hipError_t launch_scales_to_gemm(const uint8_t* s, int64_t batch, int64_t rows, 
 hipError_t launch_quant_32x32(const uint16_t* x, int64_t rows_total, int64_t cols, uint8_t* q, uint8_t* s,
                               hipStream_t st);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t st);
+// status[0] = validity bitmask of the group offsets (see mx_check_offsets).
+hipError_t launch_check_offsets(const int32_t* offs, int64_t E, int64_t M, int align, int32_t* status,
+                                hipStream_t st);
 size_t gemm_lds_bytes();
 
 constexpr int kMaxExperts = 1024;

@@ -125,7 +125,9 @@ __global__ __launch_bounds__(kRowThreads) void quant_rowwise_gather_kernel(const
 }
 
 // ---------------------------------------------------------------------------
-// Colwise: x [batch, rows, cols] -> q_t [batch, cols, ldq], s_t (ldq >= rows).
+// Colwise: x [batch, rows, cols] -> q_t [batch, cols, ldq], s_t (ldq >= rows,
+// ldq % 32 == 0).  Columns [rows, min(ldq, rows rounded up to 128)) of q_t are
+// the codes of zero rows (0x00, scale byte 0x00).
 // A workgroup stages a 128x128 bf16 tile in LDS (coalesced 256-byte row
 // segments); wave w quantizes rows [32w, 32w+32) of the tile: lane l owns
 // columns 2l and 2l+1 and reads its 32 dwords conflict-free (one LDS row per
@@ -201,7 +203,9 @@ __global__ __launch_bounds__(256) void quant_colwise_kernel(const uint16_t* __re
     const int p = j * 256 + tid;
     const int orow = p >> 3, pc = p & 7;
     const int64_t col = c0 + orow, rr = r0 + 16 * pc;
-    if (col < cols && rr < rows) {
+    // rows past the input read as zeros: with ldq > rows the padding columns
+    // of q_t get zero codes (up to the last 128-row tile)
+    if (col < cols && rr < ldq) {
       const v4i w = *(const v4i*)(o8 + orow * kColPitch + 16 * pc);
       *(v4i*)(q_t + (b * cols + col) * ldq + rr) = w;
     }
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(256) void quant_colwise_kernel(const uint16_t* __re
   // scales: thread t < 128 owns output row c0 + t and its (up to) 4 blocks
   if (tid < kColTile) {
     const int64_t col = c0 + tid;
-    const int64_t nblk = min((int64_t)4, (rows - r0) >> 5);   // rows % 32 == 0
+    const int64_t nblk = min((int64_t)4, (ldq - r0) >> 5);    // ldq % 32 == 0
     if (col < cols) {
       const uint32_t w4 = *(const uint32_t*)(sc + tid * 4);
       if (gemm_layout) {

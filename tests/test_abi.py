@@ -73,14 +73,20 @@ def test_quantize_validation_errors():
 def test_gemm_validation_errors():
     lib = _lib()
     f = lib.mx_grouped_gemm_mx
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 64, 64, 128, 1, FAKE, None) == 2       # bad mode
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 64, 96, 1, FAKE, None) == 2        # Kc % 128
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 60, 128, 1, FAKE, None) == 2       # J % 8
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 64, 128, 0, FAKE, None) == 2       # E < 1
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 64, 128, 5000, FAKE, None) == 2    # E too large
-    assert f(FAKE, FAKE, None, FAKE, FAKE, 0, 64, 64, 128, 1, FAKE, None) == 1       # null Y
-    assert f(FAKE, FAKE, FAKE + 4, FAKE, FAKE, 0, 64, 64, 128, 1, FAKE, None) == 3   # misaligned Y
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 64, (1 << 23) + 128, 1, FAKE, None) == 2   # Kc too large
+    G = mx.SCALES_GEMM
+    assert f(FAKE, FAKE, FAKE, FAKE, G, FAKE, 2, 64, 64, 128, 1, FAKE, None) == 2       # bad mode
+    assert f(FAKE, FAKE, FAKE, FAKE, G, FAKE, 0, 64, 64, 96, 1, FAKE, None) == 2        # Kc % 128
+    assert f(FAKE, FAKE, FAKE, FAKE, G, FAKE, 0, 64, 60, 128, 1, FAKE, None) == 2       # J % 8
+    assert f(FAKE, FAKE, FAKE, FAKE, G, FAKE, 0, 64, 64, 128, 0, FAKE, None) == 2       # E < 1
+    assert f(FAKE, FAKE, FAKE, FAKE, G, FAKE, 0, 64, 64, 128, 5000, FAKE, None) == 2    # E too large
+    assert f(FAKE, FAKE, None, FAKE, G, FAKE, 0, 64, 64, 128, 1, FAKE, None) == 1       # null Y
+    assert f(FAKE, FAKE, FAKE + 4, FAKE, G, FAKE, 0, 64, 64, 128, 1, FAKE, None) == 3   # misaligned Y
+    assert f(FAKE, FAKE, FAKE, FAKE, G, FAKE, 0, 64, 64, (1 << 23) + 128, 1, FAKE, None) == 2   # Kc too large
+    # the GEMM reads only its blocked scale layout: row-major scales are refused
+    for fn in (lib.mx_grouped_gemm_mx, lib.mx_grouped_gemm_mx_f32):
+        assert fn(FAKE, FAKE, FAKE, FAKE, mx.SCALES_ROWMAJOR, FAKE, 0, 64, 64, 128, 1, FAKE, None) == 6
+        assert "mx_scales_to_gemm_layout" in _err(lib)
+        assert fn(FAKE, FAKE, FAKE, FAKE, 7, FAKE, 0, 64, 64, 128, 1, FAKE, None) == 6
     g = lib.mx_grouped_mm_fwd
     need = lib.mx_grouped_mm_workspace_bytes(0, 256, 512, 256, 2)
     assert need >= 256 * 256 + 2 * 512 * 256
@@ -178,3 +184,14 @@ def test_differentiable_primitive_rejects_bad_contracts():
         mx.mx_grouped_mm(torch.zeros((64, 128)), torch.zeros((1, 128, 128), dtype=bf), offs)
     with pytest.raises(ValueError, match="one entry per expert"):
         mx.mx_grouped_mm(torch.zeros((64, 128), dtype=bf), torch.zeros((2, 128, 128), dtype=bf), offs)
+
+
+def test_offsets_check_validates_arguments():
+    lib = _lib()
+    c = lib.mx_check_offsets
+    assert c(FAKE, 0, 64, 32, FAKE, None) == 2           # E < 1
+    assert c(FAKE, 2, -1, 32, FAKE, None) == 2           # M < 0
+    assert c(FAKE, 2, 64, 0, FAKE, None) == 2            # align < 1
+    assert c(None, 2, 64, 32, FAKE, None) == 1           # null offsets
+    assert c(FAKE, 2, 64, 32, FAKE + 2, None) == 3       # misaligned status
+

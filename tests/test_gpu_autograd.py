@@ -126,3 +126,19 @@ def test_dense_linear_is_one_expert():
         rep = oracle.r1_check(bf16_host_bits(got.detach()), ref, abs_terms=absr)
         assert rep["ok"], (name, rep)
     assert w.grad.shape == (N, K)
+
+
+def test_autograd_rejects_unaligned_group_starts():
+    """A group starting off a multiple of 32 would make the weight gradient's
+    32-token blocks straddle two experts: the primitive refuses it before any
+    GEMM, with a message naming the rule."""
+    torch = require_gpu()
+    import mxfp8_block_scaled_06_amd as mx
+    A = to_dev_bf16(inp.random_bf16((128, 128), seed=1300))
+    W = to_dev_bf16(inp.random_bf16((2, 128, 128), seed=1301, std=0.02))
+    with pytest.raises(ValueError, match="multiple of 32"):
+        mx.mx_grouped_mm(A, W, to_dev_i32(np.array([40, 128], dtype=np.int32)))
+    with pytest.raises(ValueError, match="last offset"):
+        mx.mx_grouped_mm(A, W, to_dev_i32(np.array([64, 96], dtype=np.int32)))
+    out = mx.mx_grouped_mm(A, W, to_dev_i32(np.array([64, 128], dtype=np.int32)))
+    assert out.shape == (128, 128)
