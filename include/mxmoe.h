@@ -280,6 +280,22 @@ mx_status mx_grouped_mm_dgrad_q(const uint16_t* dOut, const uint8_t* qWt, const 
                                 const int32_t* offs, int64_t M, int64_t N, int64_t K, int64_t E,
                                 uint16_t* dA, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * mx_grouped_mm_fwd_q without a workspace, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments as mx_grouped_mm_fwd_q minus the workspace,
+ * same kernels and bit-identical results.  The MX codes and scales of A go
+ * to a static device array of MX_NOALLOC_SCRATCH_BYTES (128 MiB) that the
+ * library holds on every GPU it runs on until the process ends; inputs whose
+ * quantized activations do not fit (256-aligned M*K codes plus M*K/32 scale
+ * bytes) return MX_ERR_WORKSPACE.  Nothing is allocated or freed.  Every call
+ * on one GPU shares that array: calls that overlap on one GPU (two streams,
+ * or two host threads) race and must be ordered by the caller. */
+#define MX_NOALLOC_SCRATCH_BYTES (128u << 20)
+mx_status mx_grouped_mm_fwd_q_noalloc(const uint16_t* A, const uint8_t* qW, const uint8_t* sW,
+                                      const int32_t* offs, int64_t M, int64_t N, int64_t K, int64_t E,
+                                      uint16_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

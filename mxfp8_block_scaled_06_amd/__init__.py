@@ -22,12 +22,13 @@ __all__ = [
     "mx_quantize_weights", "mx_quantize_dual", "mx_quantize_rowwise_gather",
     "mx_grouped_mm_fwd_q", "mx_grouped_mm_dgrad_q", "mx_grouped_mm", "mx_linear",
     "OP_FWD", "OP_DGRAD", "OP_WGRAD", "OP_FWD_Q", "OP_DGRAD_Q", "SCALES_ROWMAJOR", "SCALES_GEMM",
-    "mx_check_offsets", "check_offsets",
+    "mx_check_offsets", "check_offsets", "mx_grouped_mm_fwd_q_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 OP_FWD, OP_DGRAD, OP_WGRAD, OP_FWD_Q, OP_DGRAD_Q = 0, 1, 2, 3, 4
 SCALES_ROWMAJOR, SCALES_GEMM = 0, 1
 OFFS_DECREASING, OFFS_RANGE, OFFS_LAST, OFFS_ALIGN = 1, 2, 4, 8
+NOALLOC_SCRATCH_BYTES = 128 << 20     # MX_NOALLOC_SCRATCH_BYTES of include/mxmoe.h
 _STATUS = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN", 4: "MX_ERR_WORKSPACE",
            5: "MX_ERR_HIP", 6: "MX_ERR_LAYOUT"}
 
@@ -87,6 +88,8 @@ def load_library():
         f = getattr(lib, name)
         f.restype = c_int
         f.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]
+    lib.mx_grouped_mm_fwd_q_noalloc.restype = c_int
+    lib.mx_grouped_mm_fwd_q_noalloc.argtypes = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp]
     _lib = lib
     return lib
 
@@ -457,6 +460,34 @@ def check_offsets(offs, M: int, align: int = 1):
                                       (OFFS_ALIGN, f"a group starts off a multiple of {align} (pad every group "
                                                    f"with zero rows to a multiple of {align})")) if bits & bit]
         raise ValueError("invalid group offsets: " + "; ".join(why))
+
+
+def mx_grouped_mm_fwd_q_noalloc(A, qW, sW, offs, out):
+    """mx_grouped_mm_fwd_q without a workspace: the library quantizes A into a
+    static device array (NOALLOC_SCRATCH_BYTES) instead, so nothing is
+    allocated (for graph capture or loops that cannot allocate).  `out` bf16
+    [M, N] is the caller's.  Calls overlapping on one GPU share the array and
+    race."""
+    import torch
+    lib = load_library()
+    _require(A, torch.bfloat16, "A")
+    _require(qW, torch.uint8, "qW")
+    _require(sW, torch.uint8, "sW")
+    _require(offs, torch.int32, "offs")
+    M, K = A.shape
+    E, N, K2 = qW.shape
+    if K2 != K:
+        raise ValueError(f"A has K={K} but qW has K={K2}")
+    _offs(offs, E)
+    if tuple(sW.shape) != (E, K // 128, N, 4):
+        raise ValueError(f"sW must be in the GEMM scale layout {(E, K // 128, N, 4)}, got {tuple(sW.shape)}")
+    if out is None:
+        raise ValueError("out must be given: this entry point allocates nothing")
+    out = _out(out, (M, N), torch.bfloat16, A.device, "out")
+    _check("mx_grouped_mm_fwd_q_noalloc",
+           lib.mx_grouped_mm_fwd_q_noalloc(_ptr(A), _ptr(qW), _ptr(sW), _ptr(offs), M, N, K, E, _ptr(out),
+                                           _stream(A.device)))
+    return out
 
 
 def mx_grouped_mm(A, W, offs, check_offsets: bool = True):

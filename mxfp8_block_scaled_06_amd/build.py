@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmxmoe.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["mx_quant.hip", "mx_gemm.hip", "mx_route.hip", "mx_api.cpp"]
+SOURCES = ["mx_quant.hip", "mx_gemm.hip", "mx_route.hip", "mx_noalloc.hip", "mx_api.cpp"]
 
 # -packed-fp32-ops: never emit packed fp32 VALU instructions.
 HIP_FLAGS = [

@@ -117,6 +117,11 @@ mx_status check_mm(const char* fn, const void* a, const void* b, const void* off
 
 }  // namespace
 
+mx_status mxk::set_last_error(mx_status st, const char* text) {
+  g_last_error = text;
+  return st;
+}
+
 extern "C" {
 
 const char* mx_last_error(void) { return g_last_error.c_str(); }

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "mxmoe.h"
+
 namespace mxk {
 
 // Grouped GEMM arguments (see mx_gemm.hip for the operation).
@@ -53,5 +55,8 @@ hipError_t launch_check_offsets(const int32_t* offs, int64_t E, int64_t M, int a
 size_t gemm_lds_bytes();
 
 constexpr int kMaxExperts = 1024;
+
+// Record `text` as the calling thread's mx_last_error() and return `st`.
+mx_status set_last_error(mx_status st, const char* text);
 
 }  // namespace mxk

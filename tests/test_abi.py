@@ -195,3 +195,13 @@ def test_offsets_check_validates_arguments():
     assert c(None, 2, 64, 32, FAKE, None) == 1           # null offsets
     assert c(FAKE, 2, 64, 32, FAKE + 2, None) == 3       # misaligned status
 
+
+
+def test_noalloc_forward_refuses_sizes_past_its_scratch():
+    """The allocation-free forward checks its static scratch limit before any
+    device call: too many activations give MX_ERR_WORKSPACE and a clear text."""
+    lib = _lib()
+    f = lib.mx_grouped_mm_fwd_q_noalloc
+    assert f(FAKE, FAKE, FAKE, FAKE, 1 << 20, 128, 1024, 1, FAKE, None) == 4
+    assert "static scratch" in _err(lib)
+    assert f(FAKE, FAKE, FAKE, FAKE, -1, 128, 1024, 1, FAKE, None) == 2
