@@ -229,6 +229,61 @@ mx_status mx_quantize_rowwise_gather(const uint16_t* x, int64_t src_rows, const 
                                      int64_t cols, uint8_t* q, uint8_t* s_gemm, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Routed experts end to end on the device: the grouped GEMMs above take the
+ * tokens already grouped by expert, with every group padded to a multiple of
+ * 32 rows ("MXFP8 training for MoEs", section "Is MXFP8 Training for MoEs
+ * Actually Stable?": the scaled grouped GEMM over each expert's routed
+ * tokens; the MoK expert PR: routed-expert precision path).  The three calls
+ * below build that grouping from the router's expert ids, gather the tokens
+ * into it inside the quantizer, and scatter GEMM rows back to token order in
+ * the GEMM's epilogue, so no permuted bf16 copy of the tokens exists.
+ * ------------------------------------------------------------------------ */
+
+/* Grouping of n routed items (tokens of a top-1 router, or the token-expert
+ * pairs of a top-k router flattened token-major, item = token * k + slot).
+ * expert_idx int32 [n] (device): the expert of each item.  Each expert's
+ * items form one group, in their original order, followed by zero rows up to
+ * a multiple of 32.  Outputs (device):
+ *   offs [E]   int32 cumulative END offsets of the padded groups (the
+ *              grouped GEMMs' offsets; offs[E-1] <= cap);
+ *   rows [cap] int32 grouped row -> item; -1 for padding rows and for every
+ *              row past offs[E-1];
+ *   pos  [n]   int32 item -> grouped row (-1 for an item not routed);
+ *   status     one int32: 0, or 1 when some expert id lies outside [0, E)
+ *              (such items join no group).
+ * Requires 1 <= E <= 1024, 0 <= n < 2^30 and cap >= n + 31*E (the most rows
+ * the padded groups can take; round it up to a multiple of 128 to use the
+ * rows as the wgrad contraction).  Deterministic: one workgroup. */
+mx_status mx_route(const int32_t* expert_idx, int64_t n, int64_t E, int64_t cap, int32_t* offs, int32_t* rows,
+                   int32_t* pos, int32_t* status, void* stream);
+
+/* mx_quantize_dual on gathered rows: row r of the quantized operand is
+ * x[rows[r] / topk, :], or a zero row where rows[r] is negative or
+ * >= src_rows * topk.  x bf16 [src_rows, cols]; rows int32 [M] (the `rows`
+ * of mx_route, or its first M entries); outputs as mx_quantize_dual with
+ * rows = M: q [M, cols], s [cols/128, M, 4], q_t [cols, ldq] (32x1 blocks
+ * along the grouped rows), s_t [ldq/128, cols, 4].  topk = 1 gathers per
+ * item (dOut of the backward, one row per item); topk = k gathers the token
+ * of item a = token * k + slot (the forward's tokens).  Requires M % 32 == 0,
+ * cols % 128 == 0, ldq % 128 == 0, ldq >= M, 1 <= topk <= 1024 and
+ * src_rows * topk < 2^31.  Bit-identical to gathering the rows and calling
+ * mx_quantize_dual. */
+mx_status mx_quantize_dual_gather(const uint16_t* x, int64_t src_rows, const int32_t* rows, int64_t topk, int64_t M,
+                                  int64_t cols, int64_t ldq, uint8_t* q, uint8_t* s, uint8_t* q_t, uint8_t* s_t,
+                                  void* stream);
+
+/* mx_grouped_gemm_mx in mode 0 with its rows stored through a map: the
+ * result row of grouped row i (i inside a group) goes to C row row_map[i]
+ * when 0 <= row_map[i] < c_rows and is dropped otherwise; C rows no entry
+ * names are left as they were.  C bf16 [c_rows, J]; row_map int32 [I].
+ * With the `rows` of mx_route as the map, the forward's output and the
+ * dgrad's input gradient land in item order.  Arguments and rules otherwise
+ * as mx_grouped_gemm_mx (mode 0). */
+mx_status mx_grouped_gemm_mx_rows(const uint8_t* X, const uint8_t* sX, const uint8_t* Y, const uint8_t* sY,
+                                  int scale_layout, const int32_t* offs, int64_t I, int64_t J, int64_t Kc, int64_t E,
+                                  const int32_t* row_map, uint16_t* C, int64_t c_rows, void* stream);
+
+/* ------------------------------------------------------------------------
  * Prequantized expert weights: the weight 4-tuple of the MoK expert PR
  * review (weight_fp8 / weight_scale feed the forward, weight_t_fp8 /
  * weight_t_scale the backward).  Weights change once per optimizer step, so

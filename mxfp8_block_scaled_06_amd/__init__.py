@@ -23,6 +23,7 @@ __all__ = [
     "mx_grouped_mm_fwd_q", "mx_grouped_mm_dgrad_q", "mx_grouped_mm", "mx_linear",
     "OP_FWD", "OP_DGRAD", "OP_WGRAD", "OP_FWD_Q", "OP_DGRAD_Q", "SCALES_ROWMAJOR", "SCALES_GEMM",
     "mx_check_offsets", "check_offsets", "mx_grouped_mm_fwd_q_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "mx_route", "route_capacity", "mx_quantize_dual_gather", "mx_grouped_gemm_mx_rows", "mx_routed_experts",
 ]
 
 OP_FWD, OP_DGRAD, OP_WGRAD, OP_FWD_Q, OP_DGRAD_Q = 0, 1, 2, 3, 4
@@ -68,6 +69,14 @@ def load_library():
         f = getattr(lib, name)
         f.restype = c_int
         f.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, c_vp, c_int, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp]
+    lib.mx_grouped_gemm_mx_rows.restype = c_int
+    lib.mx_grouped_gemm_mx_rows.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp,
+                                            c_vp, c_i64, c_vp]
+    lib.mx_route.restype = c_int
+    lib.mx_route.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]
+    lib.mx_quantize_dual_gather.restype = c_int
+    lib.mx_quantize_dual_gather.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp,
+                                            c_vp]
     lib.mx_check_offsets.restype = c_int
     lib.mx_check_offsets.argtypes = [c_vp, c_i64, c_i64, ctypes.c_int32, c_vp, c_vp]
     lib.mx_scales_to_gemm_layout.restype = c_int
@@ -220,6 +229,17 @@ def mx_grouped_gemm_mx(X, sX, Y, sY, offs, mode: int, out=None, out_dtype=None, 
         out_dtype = out.dtype if out is not None else torch.bfloat16
     if out_dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    I, J, Kc, E, layout = _gemm_operands(X, sX, Y, sY, offs, mode, scale_layout)
+    out = _out(out, (I, J) if mode == 0 else (E, I, J), out_dtype, X.device, "out")
+    name = "mx_grouped_gemm_mx" if out_dtype == torch.bfloat16 else "mx_grouped_gemm_mx_f32"
+    _check(name, getattr(lib, name)(_ptr(X), _ptr(sX), _ptr(Y), _ptr(sY), layout, _ptr(offs), mode, I, J, Kc, E,
+                                    _ptr(out), _stream(X.device)))
+    return out
+
+
+def _gemm_operands(X, sX, Y, sY, offs, mode, scale_layout):
+    """Shape checks of the GEMM operands; returns (I, J, Kc, E, layout code)."""
+    import torch
     if scale_layout not in ("gemm", "rowmajor"):
         raise ValueError("scale_layout must be 'gemm' or 'rowmajor'")
     for t, n in ((X, "X"), (sX, "sX"), (Y, "Y"), (sY, "sY")):
@@ -245,11 +265,29 @@ def mx_grouped_gemm_mx(X, sX, Y, sY, offs, mode: int, out=None, out_dtype=None, 
                 hint = (" (these are row-major scales: convert them with mx_scales_to_gemm_layout)"
                         if t.dim() == len(want) - 1 and t.shape[-1] == Kc // 32 else "")
                 raise ValueError(f"{n} must be in the GEMM scale layout {want}, got {tuple(t.shape)}{hint}")
-    out = _out(out, (I, J) if mode == 0 else (E, I, J), out_dtype, X.device, "out")
-    name = "mx_grouped_gemm_mx" if out_dtype == torch.bfloat16 else "mx_grouped_gemm_mx_f32"
-    layout = SCALES_GEMM if scale_layout == "gemm" else SCALES_ROWMAJOR
-    _check(name, getattr(lib, name)(_ptr(X), _ptr(sX), _ptr(Y), _ptr(sY), layout, _ptr(offs), mode, I, J, Kc, E,
-                                    _ptr(out), _stream(X.device)))
+    return I, J, Kc, E, SCALES_GEMM if scale_layout == "gemm" else SCALES_ROWMAJOR
+
+
+def mx_grouped_gemm_mx_rows(X, sX, Y, sY, offs, row_map, c_rows: Optional[int] = None, out=None):
+    """mx_grouped_gemm_mx (mode 0, bf16) storing grouped row i to out row
+    row_map[i] (rows whose entry lies outside [0, c_rows) are dropped; out
+    rows no entry names are left as they were).  row_map int32 [I] on the GPU
+    (the `rows` of mx_route); out bf16 [c_rows, J] (default c_rows: out's
+    rows, else I; a new out starts at zero)."""
+    import torch
+    lib = load_library()
+    I, J, Kc, E, layout = _gemm_operands(X, sX, Y, sY, offs, 0, "gemm")
+    _require(row_map, torch.int32, "row_map")
+    if tuple(row_map.shape) != (I,):
+        raise ValueError(f"row_map must be int32 [{I}] (one entry per row of X), got {tuple(row_map.shape)}")
+    if c_rows is None:
+        c_rows = out.shape[0] if out is not None else I
+    if out is None:
+        out = torch.zeros((c_rows, J), dtype=torch.bfloat16, device=X.device)
+    out = _out(out, (c_rows, J), torch.bfloat16, X.device, "out")
+    _check("mx_grouped_gemm_mx_rows",
+           lib.mx_grouped_gemm_mx_rows(_ptr(X), _ptr(sX), _ptr(Y), _ptr(sY), layout, _ptr(offs), I, J, Kc, E,
+                                       _ptr(row_map), _ptr(out), int(c_rows), _stream(X.device)))
     return out
 
 
@@ -490,10 +528,11 @@ def mx_grouped_mm_fwd_q_noalloc(A, qW, sW, offs, out):
     return out
 
 
-def mx_grouped_mm(A, W, offs, check_offsets: bool = True):
-    """Differentiable MXFP8 grouped GEMM (forward, dgrad, wgrad in the library's kernels)."""
+def mx_grouped_mm(A, W, offs, check_offsets: bool = True, weights=None, cache=None):
+    """Differentiable MXFP8 grouped GEMM (forward, dgrad, wgrad in the library's kernels);
+    expert weights quantized once and cached across micro-batches until they change."""
     from .autograd import mx_grouped_mm as _f
-    return _f(A, W, offs, check_offsets)
+    return _f(A, W, offs, check_offsets, weights, cache)
 
 
 def mx_linear(x, weight):
@@ -516,3 +555,71 @@ def mx_quantize_rowwise_gather(x, rows, q=None, s=None):
     _check("mx_quantize_rowwise_gather",
            lib.mx_quantize_rowwise_gather(_ptr(x), src_rows, _ptr(rows), M, cols, _ptr(q), _ptr(s), _stream(x.device)))
     return q, s
+
+
+# ---------------------------------------------------------------------------
+# Routed experts: grouping, gather and scatter on the device
+# ---------------------------------------------------------------------------
+def route_capacity(n: int, E: int) -> int:
+    """Rows of the grouped operands for n routed items over E experts: the
+    most the groups can take once each is padded to 32 rows (n + 31 E),
+    rounded up to 128 so the rows also serve as the wgrad contraction."""
+    return (int(n) + 31 * int(E) + 127) // 128 * 128
+
+
+def mx_route(expert_idx, E: int, cap: Optional[int] = None, offs=None, rows=None, pos=None, status=None):
+    """Group routed items by expert on the device.  expert_idx int32 [n] (a
+    top-k router's [T, k] ids flattened token-major).  Returns (offs int32 [E]
+    padded END offsets, rows int32 [cap] grouped row -> item or -1, pos int32
+    [n] item -> grouped row, status int32 [1]: 1 if an id lies outside
+    [0, E)).  Nothing is synchronized."""
+    import torch
+    lib = load_library()
+    _require(expert_idx, torch.int32, "expert_idx")
+    if expert_idx.dim() != 1:
+        raise ValueError("expert_idx must be int32 [n] (flatten a [T, k] router output)")
+    n = expert_idx.shape[0]
+    if cap is None:
+        cap = route_capacity(n, E)
+    dev = expert_idx.device
+    offs = _out(offs, (E,), torch.int32, dev, "offs")
+    rows = _out(rows, (cap,), torch.int32, dev, "rows")
+    pos = _out(pos, (n,), torch.int32, dev, "pos")
+    status = _out(status, (1,), torch.int32, dev, "status")
+    _check("mx_route", lib.mx_route(_ptr(expert_idx), n, int(E), int(cap), _ptr(offs), _ptr(rows), _ptr(pos),
+                                    _ptr(status), _stream(dev)))
+    return offs, rows, pos, status
+
+
+def mx_quantize_dual_gather(x, rows, topk: int = 1, ldq: Optional[int] = None, q=None, s=None, q_t=None, s_t=None):
+    """mx_quantize_dual of the gathered rows x[rows[r] // topk] (zero rows
+    where rows[r] < 0 or >= x.shape[0] * topk).  rows int32 [M] (M % 32 == 0).
+    Returns (q [M, cols], s [cols/128, M, 4], q_t [cols, ldq], s_t
+    [ldq/128, cols, 4]); ldq defaults to M rounded up to 128."""
+    import torch
+    lib = load_library()
+    _require(x, torch.bfloat16, "x")
+    _require(rows, torch.int32, "rows")
+    if x.dim() != 2 or rows.dim() != 1:
+        raise ValueError("x must be [src_rows, cols] and rows int32 [M]")
+    src_rows, cols = x.shape
+    M = rows.shape[0]
+    if ldq is None:
+        ldq = (M + 127) // 128 * 128
+    dev = x.device
+    q = _out(q, (M, cols), torch.uint8, dev, "q")
+    s = _out(s, (cols // 128, M, 4), torch.uint8, dev, "s")
+    q_t = _out(q_t, (cols, ldq), torch.uint8, dev, "q_t")
+    s_t = _out(s_t, (ldq // 128, cols, 4), torch.uint8, dev, "s_t")
+    _check("mx_quantize_dual_gather",
+           lib.mx_quantize_dual_gather(_ptr(x), src_rows, _ptr(rows), int(topk), M, cols, int(ldq), _ptr(q), _ptr(s),
+                                       _ptr(q_t), _ptr(s_t), _stream(dev)))
+    return q, s, q_t, s_t
+
+
+def mx_routed_experts(x, expert_idx, W, check: bool = True, weights=None, cache=None):
+    """Differentiable routed experts: out[t] = x[t] @ W[expert_idx[t]]^T, with
+    the grouping, the token gather (inside the quantizer) and the scatter
+    back to token order (inside the GEMM epilogue) on the device."""
+    from .autograd import mx_routed_experts as _f
+    return _f(x, expert_idx, W, check, weights, cache)

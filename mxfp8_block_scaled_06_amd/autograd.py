@@ -6,8 +6,10 @@ is the primitive of the "MXFP8 training for MoEs" article (section "Is MXFP8
 Training for MoEs Actually Stable?": dynamic MXFP8 quantization, scaled
 grouped GEMM, result in the original precision, differentiable; section "Why
 Does MXFP8 Speed Up MoE Training So Much?": the backward mirrors the forward).
-The forward quantizes the expert weights once in both orientations and keeps
-the one the backward needs: the weight 4-tuple of the MoK expert PR review.
+The expert weights are quantized once in both orientations (the weight
+4-tuple of the MoK expert PR review) and cached until they change, so the
+micro-batches of one optimizer step share one weight quantization; the
+forward keeps the orientation the backward needs.
 Activations get the same treatment: the forward quantizes A in both
 orientations from one read (1x32 along K for its own GEMM, 32x1 along the
 tokens for the wgrad GEMM) and keeps the fp8 transpose instead of the bf16 A;
@@ -28,8 +30,69 @@ check_offsets=False):
 
 from __future__ import annotations
 
-from . import (mx_grouped_gemm_mx, mx_grouped_mm_dgrad_q, mx_grouped_mm_fwd_q, mx_quantize_dual,
-               mx_quantize_weights)
+import weakref
+
+from . import (mx_grouped_gemm_mx, mx_grouped_gemm_mx_rows, mx_grouped_mm_dgrad_q, mx_grouped_mm_fwd_q,
+               mx_quantize_dual, mx_quantize_dual_gather, mx_quantize_rowwise_gather, mx_quantize_weights,
+               mx_route)
+
+
+class WeightCache:
+    """Prequantized expert weights kept across micro-batches until the weights
+    change: the weight cache of the "feat(moe): add MoK MXFP8 expert support"
+    PR review (keyed by storage identity, reused until optimizer.step()).
+
+    An entry holds the MX 4-tuple (q, s, q_t, s_t) of mx_quantize_weights for
+    one weight tensor and is valid while that same tensor object is alive, at
+    the same storage and shape, with the same in-place version counter: an
+    optimizer step updates the weights in place, which bumps the counter, so
+    the next forward quantizes them again.  `quantizations` counts the
+    quantization passes run (tests use it)."""
+
+    def __init__(self):
+        self._entries = {}
+        self.quantizations = 0
+
+    @staticmethod
+    def _key(W):
+        return (W.data_ptr(), tuple(W.shape), tuple(W.stride()), W.device, W._version)
+
+    def get(self, W, as_experts=None):
+        """The 4-tuple of W (or of `as_experts`, a 3-D view of W such as a
+        dense weight's unsqueeze(0), while the entry stays keyed on W)."""
+        ent = self._entries.get(id(W))
+        if ent is not None and ent[0]() is W and ent[1] == self._key(W):
+            return ent[2]
+        # quantized from a detached view: the 4-tuple is not part of the autograd graph
+        mx4 = mx_quantize_weights((W if as_experts is None else as_experts).detach())
+        self.quantizations += 1
+        self._entries[id(W)] = (weakref.ref(W, lambda _, k=id(W): self._entries.pop(k, None)), self._key(W), mx4)
+        return mx4
+
+    def clear(self):
+        self._entries.clear()
+
+
+_DEFAULT_CACHE = WeightCache()
+
+
+def weight_cache() -> WeightCache:
+    """The cache mx_grouped_mm uses unless told otherwise."""
+    return _DEFAULT_CACHE
+
+
+def _check_mx4(W, mx4):
+    """The prequantized 4-tuple must match W's shape; a mismatch raises (the
+    MoK contract: the FP8 weights are given exactly when they are used)."""
+    import torch
+    E, N, K = W.shape
+    want = ((E, N, K), (E, K // 128, N, 4), (E, K, N), (E, N // 128, K, 4))
+    if len(mx4) != 4:
+        raise ValueError("mx_grouped_mm: weights must be the 4-tuple (q, s, q_t, s_t) of mx_quantize_weights")
+    for t, sh, name in zip(mx4, want, ("q", "s", "q_t", "s_t")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or tuple(t.shape) != sh:
+            raise ValueError(f"mx_grouped_mm: prequantized weights {name} must be uint8 {sh}, got "
+                             f"{getattr(t, 'dtype', type(t))} {tuple(getattr(t, 'shape', ()))}")
 
 
 def _check(A, W, offs, check_offsets=True):
@@ -67,8 +130,8 @@ class _MXGroupedMM:
 
             class Fn(torch.autograd.Function):
                 @staticmethod
-                def forward(ctx, A, W, offs):
-                    qW, sW, qWt, sWt = mx_quantize_weights(W)
+                def forward(ctx, A, W, offs, mx4):
+                    qW, sW, qWt, sWt = mx4
                     if ctx.needs_input_grad[1]:
                         # A in both orientations: the 32x1-along-tokens codes
                         # are the wgrad operand, kept instead of the bf16 A
@@ -98,16 +161,27 @@ class _MXGroupedMM:
                         dW = mx_grouped_gemm_mx(qGt, sGt, qAt, sAt, offs, 1)
                     elif ctx.needs_input_grad[0]:
                         dA = mx_grouped_mm_dgrad_q(dOut, qWt, sWt, offs)
-                    return dA, dW, None
+                    return dA, dW, None, None
 
             cls.fn = Fn
         return cls.fn
 
 
-def mx_grouped_mm(A, W, offs, check_offsets: bool = True):
-    """Differentiable out[g_e] = A[g_e] @ W[e]^T with MXFP8 operands (see the module docstring)."""
+def mx_grouped_mm(A, W, offs, check_offsets: bool = True, weights=None, cache: WeightCache | None = None):
+    """Differentiable out[g_e] = A[g_e] @ W[e]^T with MXFP8 operands (see the module docstring).
+
+    The expert weights' MX 4-tuple comes from `weights` when given (the
+    caller's own prequantized copy, checked against W's shape), else from
+    `cache` (default: the module's WeightCache), which quantizes W once and
+    reuses the result across micro-batches until W changes."""
     _check(A, W, offs, check_offsets)
-    return _MXGroupedMM.get().apply(A.contiguous(), W.contiguous(), offs)
+    W = W.contiguous()
+    if weights is not None:
+        _check_mx4(W, weights)
+        mx4 = tuple(weights)
+    else:
+        mx4 = (cache if cache is not None else _DEFAULT_CACHE).get(W)
+    return _MXGroupedMM.get().apply(A.contiguous(), W, offs, mx4)
 
 
 def mx_linear(x, weight):
@@ -121,4 +195,96 @@ def mx_linear(x, weight):
     if x.dim() != 2:
         raise ValueError("mx_linear: x must be [M, K]")
     offs = torch.tensor([x.shape[0]], dtype=torch.int32, device=x.device)
-    return mx_grouped_mm(x, weight.unsqueeze(0), offs)
+    w3 = weight.unsqueeze(0)
+    return mx_grouped_mm(x, w3, offs, weights=_DEFAULT_CACHE.get(weight, as_experts=w3))
+
+
+class _MXRouted:
+    """torch.autograd.Function of mx_routed_experts (built lazily)."""
+    fn = None
+
+    @classmethod
+    def get(cls):
+        if cls.fn is None:
+            import torch
+
+            class Fn(torch.autograd.Function):
+                @staticmethod
+                def forward(ctx, x, W, offs, rows, mx4, zero_fill):
+                    qW, sW, qWt, sWt = mx4
+                    T = x.shape[0]
+                    cap = rows.shape[0]
+                    alloc = torch.zeros if zero_fill else torch.empty
+                    out = alloc((T, W.shape[1]), dtype=torch.bfloat16, device=x.device)
+                    if ctx.needs_input_grad[1]:
+                        # tokens gathered into their expert groups inside the
+                        # quantizer, in both orientations (wgrad keeps the
+                        # 32x1-along-tokens codes)
+                        qA, sA, qAt, sAt = mx_quantize_dual_gather(x, rows, ldq=cap)
+                    else:
+                        qA, sA = mx_quantize_rowwise_gather(x, rows)
+                        qAt = sAt = None
+                    # the epilogue stores each grouped row at its token's row
+                    mx_grouped_gemm_mx_rows(qA, sA, qW, sW, offs, rows, out=out)
+                    del qA, sA, qW, sW
+                    ctx.zero_fill = zero_fill
+                    ctx.save_for_backward(offs, rows, qWt, sWt, qAt, sAt)
+                    return out
+
+                @staticmethod
+                def backward(ctx, dOut):
+                    offs, rows, qWt, sWt, qAt, sAt = ctx.saved_tensors
+                    dOut = dOut.contiguous()
+                    dx = dW = None
+                    alloc = torch.zeros if ctx.zero_fill else torch.empty
+                    if ctx.needs_input_grad[1]:
+                        qG, sG, qGt, sGt = mx_quantize_dual_gather(dOut, rows, ldq=rows.shape[0])
+                        dW = mx_grouped_gemm_mx(qGt, sGt, qAt, sAt, offs, 1)
+                    elif ctx.needs_input_grad[0]:
+                        qG, sG = mx_quantize_rowwise_gather(dOut, rows)
+                    if ctx.needs_input_grad[0]:
+                        dx = alloc((dOut.shape[0], qWt.shape[1]), dtype=torch.bfloat16, device=dOut.device)
+                        mx_grouped_gemm_mx_rows(qG, sG, qWt, sWt, offs, rows, out=dx)
+                    return dx, dW, None, None, None, None
+
+            cls.fn = Fn
+        return cls.fn
+
+
+def mx_routed_experts(x, expert_idx, W, check: bool = True, weights=None, cache: WeightCache | None = None):
+    """Differentiable top-1 routed experts: out[t] = x[t] @ W[expert_idx[t]]^T.
+
+    x bf16 [T, K] in token order; expert_idx int32 [T] on the device (the
+    router's choice per token); W bf16 [E, N, K] with N % 128 == 0 and
+    K % 128 == 0; out bf16 [T, N] in token order.  mx_route groups the tokens
+    by expert on the device (each expert's tokens in their original order,
+    padded with zero rows to a multiple of 32), the quantizer gathers the
+    tokens into that grouping, and the GEMM epilogue stores every row back at
+    its token, so neither a permuted copy of the tokens nor an unpermute pass
+    exists; the backward gathers dOut the same way.  Weights as for
+    mx_grouped_mm (`weights`, else the cache).
+
+    check=True reads the routing status (one synchronization) and raises on
+    an expert id outside [0, E).  With check=False such tokens are dropped:
+    their output rows and input gradients are zero."""
+    import torch
+    if x.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
+        raise TypeError("mx_routed_experts: x and W must be bfloat16")
+    if expert_idx.dtype != torch.int32 or expert_idx.dim() != 1 or expert_idx.shape[0] != x.shape[0]:
+        raise ValueError(f"mx_routed_experts: expert_idx must be int32 [T={x.shape[0]}] (one expert per token)")
+    if x.dim() != 2 or W.dim() != 3 or W.shape[2] != x.shape[1]:
+        raise ValueError("mx_routed_experts: x must be [T, K] and W [E, N, K]")
+    E, N, K = W.shape
+    if K % 128 or N % 128:
+        raise ValueError(f"mx_routed_experts: N={N} and K={K} must be multiples of 128")
+    offs, rows, _pos, status = mx_route(expert_idx.contiguous(), E)
+    if check:
+        if int(status.item()):
+            raise ValueError(f"mx_routed_experts: an expert id lies outside [0, {E})")
+    W = W.contiguous()
+    if weights is not None:
+        _check_mx4(W, weights)
+        mx4 = tuple(weights)
+    else:
+        mx4 = (cache if cache is not None else _DEFAULT_CACHE).get(W)
+    return _MXRouted.get().apply(x.contiguous(), W, offs, rows, mx4, not check)

@@ -167,7 +167,8 @@ namespace {
 
 mx_status grouped_gemm_impl(const char* fn, const uint8_t* X, const uint8_t* sX, const uint8_t* Y,
                             const uint8_t* sY, int scale_layout, const int32_t* offs, int mode, int64_t I, int64_t J,
-                            int64_t Kc, int64_t E, void* C, int out_f32, void* stream) {
+                            int64_t Kc, int64_t E, void* C, int out_f32, void* stream,
+                            const int32_t* row_map = nullptr, int64_t c_rows = -1) {
   if (scale_layout == MX_SCALES_ROWMAJOR)
     return fail(MX_ERR_LAYOUT,
                 "%s: the GEMM reads scales in its blocked layout [K/128][rows][4]; row-major scales "
@@ -213,6 +214,8 @@ mx_status grouped_gemm_impl(const char* fn, const uint8_t* X, const uint8_t* sX,
   a.sy_estride = J * (Kc / 32);
   a.ldc = J;
   a.c_estride = I * J;
+  a.row_map = row_map;
+  a.c_rows = row_map ? c_rows : I;
   return hip_status(mxk::launch_grouped_gemm(a, (hipStream_t)stream), fn);
 }
 
@@ -231,6 +234,35 @@ mx_status mx_grouped_gemm_mx_f32(const uint8_t* X, const uint8_t* sX, const uint
                                  int64_t E, float* C, void* stream) {
   return grouped_gemm_impl("mx_grouped_gemm_mx_f32", X, sX, Y, sY, scale_layout, offs, mode, I, J, Kc, E, C, 1,
                            stream);
+}
+
+mx_status mx_grouped_gemm_mx_rows(const uint8_t* X, const uint8_t* sX, const uint8_t* Y, const uint8_t* sY,
+                                  int scale_layout, const int32_t* offs, int64_t I, int64_t J, int64_t Kc, int64_t E,
+                                  const int32_t* row_map, uint16_t* C, int64_t c_rows, void* stream) {
+  const char* fn = "mx_grouped_gemm_mx_rows";
+  if (c_rows < 0 || c_rows >= ((int64_t)1 << 31))
+    return fail(MX_ERR_SHAPE, "%s: c_rows=%lld outside [0, 2^31)", fn, (long long)c_rows);
+  if (c_rows == 0) return MX_OK;
+  if (!row_map) return fail(MX_ERR_NULL, "%s: null row map", fn);
+  if (!aligned(row_map, 4)) return fail(MX_ERR_ALIGN, "%s: row_map must be 4-byte aligned", fn);
+  return grouped_gemm_impl(fn, X, sX, Y, sY, scale_layout, offs, 0, I, J, Kc, E, C, 0, stream, row_map, c_rows);
+}
+
+mx_status mx_route(const int32_t* expert_idx, int64_t n, int64_t E, int64_t cap, int32_t* offs, int32_t* rows,
+                   int32_t* pos, int32_t* status, void* stream) {
+  const char* fn = "mx_route";
+  if (E < 1 || E > mxk::kMaxExperts)
+    return fail(MX_ERR_SHAPE, "%s: number of experts E=%lld outside [1, %d]", fn, (long long)E, mxk::kMaxExperts);
+  if (n < 0 || n >= ((int64_t)1 << 30)) return fail(MX_ERR_SHAPE, "%s: n=%lld outside [0, 2^30)", fn, (long long)n);
+  // every group takes at most 31 padding rows
+  if (cap < n + 31 * E || cap >= ((int64_t)1 << 31))
+    return fail(MX_ERR_SHAPE, "%s: cap=%lld must be >= n + 31*E = %lld (and < 2^31)", fn, (long long)cap,
+                (long long)(n + 31 * E));
+  if ((n > 0 && (!expert_idx || !pos)) || !offs || !rows || !status)
+    return fail(MX_ERR_NULL, "%s: null pointer", fn);
+  if (!aligned(expert_idx, 4) || !aligned(offs, 4) || !aligned(rows, 4) || !aligned(pos, 4) || !aligned(status, 4))
+    return fail(MX_ERR_ALIGN, "%s: int32 arrays must be 4-byte aligned", fn);
+  return hip_status(mxk::launch_route(expert_idx, n, E, cap, offs, rows, pos, status, (hipStream_t)stream), fn);
 }
 
 mx_status mx_check_offsets(const int32_t* offs, int64_t E, int64_t M, int32_t align, int32_t* status, void* stream) {
@@ -368,6 +400,34 @@ mx_status mx_quantize_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(q_t, 16) || !aligned(s, 4) || !aligned(s_t, 4))
     return fail(MX_ERR_ALIGN, "%s: x, q, q_t must be 16-byte and s, s_t 4-byte aligned", fn);
   return hip_status(mxk::launch_quant_dual(x, 1, rows, cols, ldq, q, s, q_t, s_t, (hipStream_t)stream), fn);
+}
+
+mx_status mx_quantize_dual_gather(const uint16_t* x, int64_t src_rows, const int32_t* rows, int64_t topk, int64_t M,
+                                  int64_t cols, int64_t ldq, uint8_t* q, uint8_t* s, uint8_t* q_t, uint8_t* s_t,
+                                  void* stream) {
+  const char* fn = "mx_quantize_dual_gather";
+  if (src_rows < 0 || M < 0 || cols < 0 || ldq < 0)
+    return fail(MX_ERR_SHAPE, "%s: src_rows=%lld M=%lld cols=%lld ldq=%lld", fn, (long long)src_rows, (long long)M,
+                (long long)cols, (long long)ldq);
+  if (topk < 1 || topk > 1024) return fail(MX_ERR_SHAPE, "%s: topk=%lld outside [1, 1024]", fn, (long long)topk);
+  if (M % 32 != 0 || cols % 128 != 0)
+    return fail(MX_ERR_SHAPE, "%s: M=%lld must be a multiple of 32 and cols=%lld of 128", fn, (long long)M,
+                (long long)cols);
+  if (ldq % 128 != 0 || ldq < M)
+    return fail(MX_ERR_SHAPE, "%s: ldq=%lld must be a multiple of 128 and >= M=%lld", fn, (long long)ldq,
+                (long long)M);
+  if (src_rows * topk >= ((int64_t)1 << 31))
+    return fail(MX_ERR_SHAPE, "%s: src_rows*topk must be below 2^31", fn);
+  if (ldq == 0 || cols == 0) return MX_OK;
+  if (ldq / 128 > 65535 || cols / 128 > 65535) return fail(MX_ERR_SHAPE, "%s: too large for one launch", fn);
+  if ((M > 0 && !rows) || !q || !s || !q_t || !s_t || (src_rows > 0 && !x))
+    return fail(MX_ERR_NULL, "%s: null pointer", fn);
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(q_t, 16) || !aligned(s, 4) || !aligned(s_t, 4) ||
+      !aligned(rows, 4))
+    return fail(MX_ERR_ALIGN, "%s: x, q, q_t must be 16-byte and s, s_t, rows 4-byte aligned", fn);
+  return hip_status(mxk::launch_quant_dual(x, 1, M, cols, ldq, q, s, q_t, s_t, (hipStream_t)stream,
+                                           M > 0 ? rows : nullptr, src_rows, (int)topk),
+                    fn);
 }
 
 mx_status mx_grouped_mm_fwd_q(const uint16_t* A, const uint8_t* qW, const uint8_t* sW, const int32_t* offs, int64_t M,

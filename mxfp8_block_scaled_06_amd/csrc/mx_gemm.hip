@@ -559,6 +559,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
     for (int qx = 0; qx < 4; ++qx) {
       const int64_t i = i0 + iw * 128 + qx * 32 + l32;
       if (i >= i_lim) continue;
+      const int64_t dst = a.row_map ? (int64_t)a.row_map[i] : i;
+      if (dst < 0 || dst >= a.c_rows) continue;
 #pragma unroll
       for (int qy = 0; qy < 4; ++qy) {
 #pragma unroll
@@ -566,7 +568,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
           const int64_t j = j0 + jw * 128 + qy * 32 + 8 * g + 4 * half;
           if (j < a.J) {
             const v16f& v = acc[qy][qx];
-            float* crow = (float*)a.C + c_off + i * a.ldc;
+            float* crow = (float*)a.C + c_off + dst * a.ldc;
             *(float4*)(crow + j) = make_float4(v[4 * g + 0], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
           }
         }
@@ -622,7 +624,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
       const int row = it * 8 + (tid >> 5);
       const int64_t i = i0 + row;
       const v4i w = *(const v4i*)(ot + row * kOutPitch + c8 * 2);
-      if (i < i_lim && j < a.J) __builtin_nontemporal_store(w, (v4i*)((uint16_t*)a.C + c_off + i * a.ldc + j));
+      // with a row map (routed tokens) the row goes back to its token's place
+      const int64_t dst = i < i_lim ? (a.row_map ? (int64_t)a.row_map[i] : i) : -1;
+      if (dst >= 0 && dst < a.c_rows && j < a.J)
+        __builtin_nontemporal_store(w, (v4i*)((uint16_t*)a.C + c_off + dst * a.ldc + j));
     }
   }
 }

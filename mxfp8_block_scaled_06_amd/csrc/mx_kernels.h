@@ -26,6 +26,8 @@ struct GemmArgs {
   int64_t sy_estride;         // mode 0: bytes between experts of sY
   int64_t ldc;                // elements per row of C
   int64_t c_estride;          // mode 1: elements between experts of C
+  const int32_t* row_map;     // mode 0, optional: X row i is stored to C row row_map[i] (skipped if outside [0, c_rows))
+  int64_t c_rows;
 };
 
 // gemm_rows_per_batch == 0: row-major scales [rows_total][cols/32]; > 0:
@@ -42,13 +44,20 @@ hipError_t launch_quant_colwise(const uint16_t* x, int64_t batch, int64_t rows, 
 // Both orientations of w [E, N, K] (N % 32 == 0, K % 128 == 0, ldq % 128 == 0,
 // ldq >= N): q [E, N, K] with s in GEMM layout [E][K/128][N][4]; q_t
 // [E, K, ldq] with s_t in GEMM layout [E][ldq/128][K][4], zero past N.
+// rows != nullptr: row n of the (batch-1) input is x[rows[n] / topk] (a zero
+// row when rows[n] is negative or >= src_rows * topk): the token gather of the
+// MoE dispatch.
 hipError_t launch_quant_dual(const uint16_t* w, int64_t E, int64_t N, int64_t K, int64_t ldq, uint8_t* q,
-                             uint8_t* s, uint8_t* q_t, uint8_t* s_t, hipStream_t st);
+                             uint8_t* s, uint8_t* q_t, uint8_t* s_t, hipStream_t st,
+                             const int32_t* rows = nullptr, int64_t src_rows = 0, int topk = 1);
 hipError_t launch_scales_to_gemm(const uint8_t* s, int64_t batch, int64_t rows, int64_t kb, uint8_t* out,
                                  hipStream_t st);
 hipError_t launch_quant_32x32(const uint16_t* x, int64_t rows_total, int64_t cols, uint8_t* q, uint8_t* s,
                               hipStream_t st);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t st);
+// Routing metadata (see mx_route).
+hipError_t launch_route(const int32_t* expert_idx, int64_t T, int64_t E, int64_t cap, int32_t* offs,
+                             int32_t* rows, int32_t* pos, int32_t* status, hipStream_t st);
 // status[0] = validity bitmask of the group offsets (see mx_check_offsets).
 hipError_t launch_check_offsets(const int32_t* offs, int64_t E, int64_t M, int align, int32_t* status,
                                 hipStream_t st);

@@ -254,7 +254,9 @@ constexpr int kDualPitch = 272;   // bytes per staged input row (256 + 16): conf
 __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restrict__ w, int64_t N, int64_t K,
                                                          int64_t ldq, uint8_t* __restrict__ q,
                                                          uint8_t* __restrict__ s, uint8_t* __restrict__ q_t,
-                                                         uint8_t* __restrict__ s_t) {
+                                                         uint8_t* __restrict__ s_t,
+                                                         const int32_t* __restrict__ rows, int64_t n_items,
+                                                         uint32_t topk) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kColTile * kDualPitch];
   const int tid = threadIdx.x;
   const int64_t b = blockIdx.z;
@@ -266,7 +268,15 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
     const int chunk = it * 256 + tid;
     const int rr = chunk >> 4, cc = chunk & 15;
     v4i v = (v4i){0, 0, 0, 0};
-    if (n0 + rr < N) v = __builtin_nontemporal_load((const v4i*)(wb + (n0 + rr) * K + k0 + cc * 8));
+    if (n0 + rr < N) {
+      // gathered rows: row n of the tile is input row rows[n] / topk
+      // (negative or out of range: a zero row, the padding of an expert group)
+      const int64_t item = rows ? (int64_t)rows[n0 + rr] : n0 + rr;
+      if (item >= 0 && item < n_items) {
+        const int64_t src = topk == 1 ? item : (int64_t)((uint32_t)item / topk);
+        v = __builtin_nontemporal_load((const v4i*)(wb + src * K + k0 + cc * 8));
+      }
+    }
     *(v4i*)(tile + rr * kDualPitch + cc * 16) = v;
   }
   __syncthreads();
@@ -408,10 +418,12 @@ hipError_t launch_quant_rowwise(const uint16_t* x, int64_t rows_total, int64_t c
 }
 
 hipError_t launch_quant_dual(const uint16_t* w, int64_t E, int64_t N, int64_t K, int64_t ldq, uint8_t* q,
-                             uint8_t* s, uint8_t* q_t, uint8_t* s_t, hipStream_t st) {
+                             uint8_t* s, uint8_t* q_t, uint8_t* s_t, hipStream_t st, const int32_t* rows,
+                             int64_t src_rows, int topk) {
   if (E == 0 || ldq == 0 || K == 0) return hipSuccess;
   dim3 grid((unsigned)(K / kColTile), (unsigned)(ldq / kColTile), (unsigned)E);
-  hipLaunchKernelGGL(quant_dual_kernel, grid, dim3(256), 0, st, w, N, K, ldq, q, s, q_t, s_t);
+  hipLaunchKernelGGL(quant_dual_kernel, grid, dim3(256), 0, st, w, N, K, ldq, q, s, q_t, s_t, rows,
+                     rows ? src_rows * topk : N, (uint32_t)(rows ? topk : 1));
   return hipGetLastError();
 }
 

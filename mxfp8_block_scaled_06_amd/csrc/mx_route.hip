@@ -43,3 +43,125 @@ hipError_t launch_check_offsets(const int32_t* offs, int64_t E, int64_t M, int a
 }
 
 }  // namespace mxk
+
+namespace mxk {
+
+// ---------------------------------------------------------------------------
+// Routing metadata.  Item a (a token, or one token-expert pair of a top-k
+// router, flattened token-major) goes to expert expert_idx[a]; each expert's
+// items form one group, in their original order, padded with zero rows to a
+// multiple of 32 (the weight gradient's 32-token blocks then never straddle
+// two experts).  Outputs, all on the device:
+//   offs [E]   cumulative padded END offsets (the grouped GEMMs' offsets)
+//   rows [cap] grouped row -> item, -1 for padding and rows past the last group
+//   pos  [n]   item -> grouped row
+// status[0] gets 1 if some expert id lies outside [0, E) (those items are not
+// routed: pos = -1).  One workgroup of 1024 threads: a histogram, a scan of
+// the padded counts, then the items in chunks of 1024 in order, each item's
+// rank among the earlier items of its expert from wave ballots and a scan of
+// per-wave counts, so the result does not depend on thread timing.  The host
+// guarantees cap >= n + 31 * E, the most rows the padded groups can take.
+// ---------------------------------------------------------------------------
+constexpr int kRouteThreads = 1024;
+constexpr int kRouteWaves = kRouteThreads / 64;
+
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ expert_idx, int T, int E,
+                                                                   int cap, int32_t* __restrict__ offs,
+                                                                   int32_t* __restrict__ rows,
+                                                                   int32_t* __restrict__ pos,
+                                                                   int32_t* __restrict__ status) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int start[kMaxExperts];
+  __shared__ int run[kMaxExperts];
+  __shared__ int wc[kRouteWaves][kMaxExperts];
+  __shared__ int bad, total;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int e = tid; e < E; e += kRouteThreads) {
+    cnt[e] = 0;
+    run[e] = 0;
+  }
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  for (int t = tid; t < T; t += kRouteThreads) {
+    const int e = expert_idx[t];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    else bad = 1;
+  }
+  __syncthreads();
+  // exclusive scan of the padded counts (E <= 1024: one expert per thread)
+  {
+    const int e = tid;
+    const int pc = e < E ? (cnt[e] + 31) & ~31 : 0;
+    int incl = pc;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if (lane >= d) incl += v;
+    }
+    if (lane == 63) wc[0][wv] = incl;   // wave totals (wc reused as scratch)
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wv; ++w) before += wc[0][w];
+    if (e < E) {
+      start[e] = before + incl - pc;
+      offs[e] = before + incl;
+      // padding rows of this group
+      for (int r = start[e] + cnt[e]; r < before + incl; ++r) rows[r] = -1;
+    }
+    if (e == E - 1) total = before + incl;
+    __syncthreads();
+  }
+  for (int r = total + tid; r < cap; r += kRouteThreads) rows[r] = -1;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int base = 0; base < T; base += kRouteThreads) {
+    for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) wc[i / E][i % E] = 0;
+    __syncthreads();
+    const int t = base + tid;
+    const int e = t < T ? expert_idx[t] : -1;
+    const bool valid = e >= 0 && e < E;
+    int rank = 0;
+    uint64_t remaining = __ballot(valid);
+    while (remaining) {
+      const int leader = __builtin_ctzll(remaining);
+      const int le = __shfl(e, leader);
+      const uint64_t m = __ballot(valid && e == le);
+      if (valid && e == le) {
+        rank = __builtin_popcountll(m & lt);
+        if (lane == leader) wc[wv][le] = __builtin_popcountll(m);
+      }
+      remaining &= ~m;
+    }
+    __syncthreads();
+    // per expert: earlier waves of this chunk, plus earlier chunks
+    for (int x = tid; x < E; x += kRouteThreads) {
+      int acc = run[x];
+      for (int w = 0; w < kRouteWaves; ++w) {
+        const int c = wc[w][x];
+        wc[w][x] = acc;
+        acc += c;
+      }
+      run[x] = acc;
+    }
+    __syncthreads();
+    if (t < T) {
+      if (valid) {
+        const int p = start[e] + wc[wv][e] + rank;
+        pos[t] = p;
+        rows[p] = t;
+      } else {
+        pos[t] = -1;
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) status[0] = bad;
+}
+
+hipError_t launch_route(const int32_t* expert_idx, int64_t T, int64_t E, int64_t cap, int32_t* offs,
+                             int32_t* rows, int32_t* pos, int32_t* status, hipStream_t st) {
+  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, st, expert_idx, (int)T, (int)E, (int)cap,
+                     offs, rows, pos, status);
+  return hipGetLastError();
+}
+
+}  // namespace mxk

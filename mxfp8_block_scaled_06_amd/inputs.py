@@ -78,6 +78,13 @@ def pad_counts(counts, multiple: int = 32) -> np.ndarray:
     return ((c + multiple - 1) // multiple) * multiple
 
 
+def expert_ids(rng, counts) -> np.ndarray:
+    """Router output in token order: int32 [sum(counts)] holding counts[e]
+    copies of each expert id e, in a seeded random order."""
+    ids = np.repeat(np.arange(len(counts), dtype=np.int32), np.asarray(counts, dtype=np.int64))
+    return rng.permutation(ids).astype(np.int32)
+
+
 def uniform_counts(rng, total: int, experts: int) -> np.ndarray:
     """Top-1 routing drawn from a multinomial over uniform expert probabilities."""
     return rng.multinomial(total, np.full(experts, 1.0 / experts)).astype(np.int64)

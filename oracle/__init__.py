@@ -10,3 +10,6 @@ from .mxfp8 import (  # noqa: F401
     grouped_gemm_mx, grouped_mm_fwd, grouped_mm_dgrad, grouped_mm_wgrad, group_bounds,
 )
 from .compare import r1_check, rne_bf16, ulp_bf16  # noqa: F401
+from .route import (  # noqa: F401
+    route_groups, gather_rows, scatter_rows, routed_fwd, routed_dgrad, routed_wgrad,
+)

@@ -197,6 +197,30 @@ def test_offsets_check_validates_arguments():
 
 
 
+def test_routing_entry_points_validate():
+    lib = _lib()
+    r = lib.mx_route
+    assert r(FAKE, 100, 4, 100 + 31 * 4 - 1, FAKE, FAKE, FAKE, FAKE, None) == 2     # cap below n + 31 E
+    assert "cap" in _err(lib)
+    assert r(FAKE, 100, 0, 1024, FAKE, FAKE, FAKE, FAKE, None) == 2                # E < 1
+    assert r(FAKE, 100, 1025, 1 << 16, FAKE, FAKE, FAKE, FAKE, None) == 2          # E > 1024
+    assert r(FAKE, -1, 4, 1024, FAKE, FAKE, FAKE, FAKE, None) == 2                 # n < 0
+    assert r(None, 100, 4, 1024, FAKE, FAKE, FAKE, FAKE, None) == 1                # null ids
+    assert r(FAKE, 100, 4, 1024, FAKE, FAKE + 2, FAKE, FAKE, None) == 3            # misaligned rows
+    g = lib.mx_quantize_dual_gather
+    assert g(FAKE, 10, FAKE, 0, 64, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == 2   # topk < 1
+    assert g(FAKE, 10, FAKE, 1, 48, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == 2   # M % 32
+    assert g(FAKE, 10, FAKE, 1, 64, 128, 32, FAKE, FAKE, FAKE, FAKE, None) == 2    # ldq < M
+    assert g(FAKE, 1 << 30, FAKE, 2, 64, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == 2   # src_rows*topk
+    assert g(FAKE, 10, None, 1, 64, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == 1   # null rows
+    m = lib.mx_grouped_gemm_mx_rows
+    args = (FAKE, FAKE, FAKE, FAKE, mx.SCALES_GEMM, FAKE, 256, 128, 128, 2)
+    assert m(*args, FAKE, FAKE, -1, None) == 2                                     # c_rows < 0
+    assert m(*args, None, FAKE, 10, None) == 1                                     # null map
+    assert m(*args, FAKE + 2, FAKE, 10, None) == 3                                 # misaligned map
+    assert m(FAKE, FAKE, FAKE, FAKE, mx.SCALES_ROWMAJOR, FAKE, 256, 128, 128, 2, FAKE, FAKE, 10, None) == 6
+
+
 def test_noalloc_forward_refuses_sizes_past_its_scratch():
     """The allocation-free forward checks its static scratch limit before any
     device call: too many activations give MX_ERR_WORKSPACE and a clear text."""

@@ -142,3 +142,38 @@ def test_autograd_rejects_unaligned_group_starts():
         mx.mx_grouped_mm(A, W, to_dev_i32(np.array([64, 96], dtype=np.int32)))
     out = mx.mx_grouped_mm(A, W, to_dev_i32(np.array([64, 128], dtype=np.int32)))
     assert out.shape == (128, 128)
+
+
+def test_weight_cache_spans_micro_batches_until_the_weights_change():
+    """Two micro-batches with the same expert weights run one weight
+    quantization (the prequantized-weight cache of the MoK expert PR review)
+    and give the results of quantizing every time; an in-place update of the
+    weights (what an optimizer step does) makes the next forward requantize."""
+    torch = require_gpu()
+    import mxfp8_block_scaled_06_amd as mx
+    from mxfp8_block_scaled_06_amd.autograd import WeightCache
+    counts = [64, 0, 96, 32]
+    offs = to_dev_i32(inp.offsets_from_counts(counts))
+    W = to_dev_bf16(inp.random_bf16((4, 256, 384), seed=1400, std=0.02)).requires_grad_(True)
+    cache = WeightCache()
+    outs = []
+    for mb in range(2):
+        A = to_dev_bf16(inp.random_bf16((192, 384), seed=1410 + mb, outliers=True)).requires_grad_(True)
+        out = mx.mx_grouped_mm(A, W, offs, cache=cache)
+        G = to_dev_bf16(inp.random_bf16((192, 256), seed=1420 + mb, std=1e-3))
+        out.backward(G)
+        ref = mx.mx_grouped_mm(A.detach(), W.detach(), offs, weights=mx.mx_quantize_weights(W.detach()))
+        assert torch.equal(out.detach().view(torch.int16), ref.view(torch.int16))
+        outs.append(out.detach())
+    assert cache.quantizations == 1
+    grad_after_two = W.grad.clone()
+    assert grad_after_two.abs().sum() > 0
+    with torch.no_grad():
+        W.mul_(2.0)                       # an in-place update, as an optimizer step makes
+    A = to_dev_bf16(inp.random_bf16((192, 384), seed=1410, outliers=True))
+    out = mx.mx_grouped_mm(A, W, offs, cache=cache)
+    assert cache.quantizations == 2
+    # doubling every weight doubles every scale: the result is exactly twice the first
+    assert torch.equal(out.view(torch.int16), (outs[0] * 2).view(torch.int16))
+    with pytest.raises(ValueError, match="prequantized weights"):
+        mx.mx_grouped_mm(A, W, offs, weights=mx.mx_quantize_weights(W.detach()[:, :128].contiguous()))
