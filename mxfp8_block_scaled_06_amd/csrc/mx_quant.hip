@@ -14,7 +14,11 @@
 // by 2^(127 - byte) in fp32 (exact: bf16 has 8 significant bits), clamped to
 // +-448 and converted to E4M3 with the hardware RNE convert.  All three are
 // HBM-bound streaming passes: 2 bytes read, 1 + 1/32 (or 1/1024) written per
-// element.
+// element.  Both orientations from one read (the weight 4-tuple, and the
+// activations of the differentiable step) and the colwise pass on 256-column
+// inputs run in quant_dual256_kernel, whose 256 x 256 tiles give every global
+// access 256-byte or longer runs; 128 x 128 tile kernels serve the other
+// shapes.
 #include "mx_device.h"
 #include "mx_kernels.h"
 
@@ -126,7 +130,8 @@ __global__ __launch_bounds__(kRowThreads) void quant_rowwise_gather_kernel(const
 
 // ---------------------------------------------------------------------------
 // Colwise: x [batch, rows, cols] -> q_t [batch, cols, ldq], s_t (ldq >= rows,
-// ldq % 32 == 0).  Columns [rows, min(ldq, rows rounded up to 128)) of q_t are
+// ldq % 32 == 0).  Used when cols % 256 != 0 (otherwise quant_dual256_kernel
+// without its rowwise half).  Columns [rows, min(ldq, rows rounded up to 128)) of q_t are
 // the codes of zero rows (0x00, scale byte 0x00).
 // A workgroup stages a 128x128 bf16 tile in LDS (coalesced 256-byte row
 // segments); wave w quantizes rows [32w, 32w+32) of the tile: lane l owns
@@ -240,7 +245,8 @@ __global__ __launch_bounds__(256) void quant_colwise_kernel(const uint16_t* __re
 // quantized as zero rows, so q_t's padding columns hold zero codes and zero
 // scales).  Expert weights use ldq = N; activations (the forward's A, the
 // backward's dOut) use ldq = N rounded up to 128, the contraction length of
-// the wgrad GEMM.  A workgroup stages a 128 (n) x 128 (k) bf16
+// the wgrad GEMM.  Used when K % 256 != 0 (otherwise quant_dual256_kernel).
+// A workgroup stages a 128 (n) x 128 (k) bf16
 // tile in LDS once; the rowwise half quantizes its rows straight to q (four
 // threads fill one 128-byte line), the colwise half is the colwise kernel's
 // path (column pairs, codes transposed back through LDS for whole-line
@@ -365,6 +371,161 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
 static_assert(kColTile * kColPitch + kColTile * 4 <= kColTile * kDualPitch, "output stage fits the input tile");
 
 // ---------------------------------------------------------------------------
+// Both orientations in one pass, 256 x 256 tiles (K % 256 == 0): the same
+// outputs as quant_dual_kernel with every global access twice as long.
+// 512 threads; wave w owns rows [n0 + 32w, +32) (one colwise block), lane l
+// rows n0 + 32w + 16(l/32) + i (i = 0..15) and the 16-byte piece l%32 of each
+// 512-byte row segment (8 columns).  Nothing bf16 goes through LDS:
+//  * rowwise: the four lanes of a DPP quad hold one 32-element block of a
+//    row; codes go straight to q (a wave stores two 256-byte row runs per
+//    instruction);
+//  * colwise: a lane's 16 rows and its partner lane l ^ 32's 16 rows are a
+//    whole 32-row block of its 8 columns, so the column amax is a packed
+//    16-bit max over registers plus one exchange; each column's 16 codes are
+//    one 16-byte LDS write into a [256 k][256 n] code tile (16-byte slots
+//    swizzled by k / 8 so the writes and the row reads are conflict-free),
+//    which the workgroup then stores as 256-byte runs of q_t rows;
+//  * both scale sets are staged in LDS and stored as dwords of the GEMM
+//    layout (1 KiB runs).
+// ---------------------------------------------------------------------------
+constexpr int kD2 = 256;                      // tile columns (k)
+constexpr int kD2N = 256;                     // tile rows (n)
+constexpr int kD2Threads = 2 * kD2N;
+constexpr int kD2Slots = kD2N / 16;           // 16-byte slots per code-tile row
+
+__device__ __forceinline__ int d2_slot(int k, int slot) { return slot ^ ((k >> 3) & 15); }
+
+// ROWWISE = false is the colwise quantizer alone (q and s untouched); its
+// scales go to the GEMM layout when st_ld == 0, else row-major [batch][K][st_ld]
+// (blocks n0/32 .. of row k).  128 VGPRs: two workgroups per CU.
+template <bool ROWWISE>
+__global__ __launch_bounds__(kD2Threads) __attribute__((amdgpu_waves_per_eu(4))) void quant_dual256_kernel(
+    const uint16_t* __restrict__ w, int64_t N, int64_t K, int64_t ldq, uint8_t* __restrict__ q,
+    uint8_t* __restrict__ s, uint8_t* __restrict__ q_t, uint8_t* __restrict__ s_t, int64_t st_ld,
+    const int32_t* __restrict__ rows, int64_t n_items, uint32_t topk) {
+  __shared__ __attribute__((aligned(16))) uint8_t codes[kD2 * kD2N];      // [256 k][kD2N n] transposed codes
+  __shared__ __attribute__((aligned(16))) uint8_t srow[2 * kD2N * 4];     // [k chunk][rows][4 blocks]
+  __shared__ __attribute__((aligned(16))) uint8_t scol[kD2N / 128 * kD2 * 4];   // [n chunk][256 cols][4 blocks]
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5, pc = lane & 31;
+  const int64_t b = blockIdx.z;
+  const int64_t n0 = (int64_t)blockIdx.y * kD2N;
+  const int64_t k0 = (int64_t)blockIdx.x * kD2;
+  const uint16_t* wb = w + b * N * K;
+  const int r0 = 32 * wv + 16 * half;          // tile row of this lane's i = 0
+
+  v4i v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t n = n0 + r0 + i;
+    v4i x = (v4i){0, 0, 0, 0};
+    if (n < N) {
+      // gathered rows: row n is input row rows[n] / topk (negative or out of
+      // range: a zero row, the padding of an expert group)
+      const int64_t item = rows ? (int64_t)rows[n] : n;
+      if (item >= 0 && item < n_items) {
+        const int64_t src = topk == 1 ? item : (int64_t)((uint32_t)item / topk);
+        x = __builtin_nontemporal_load((const v4i*)(wb + src * K + k0 + 8 * pc));
+      }
+    }
+    v[i] = x;
+  }
+
+  // ---- rowwise: block pc / 4 of each row
+  const int kb = pc >> 2;
+#pragma unroll
+  for (int i = 0; i < 16 && ROWWISE; ++i) {
+    const int64_t n = n0 + r0 + i;
+    const uint32_t byte = e8m0_from_absbits(quad_max(absmax8(v[i])));
+    const float m = inv_scale_from_e8m0(byte == 0xFFu ? 127u : byte);
+    const v2i c = byte == 0xFFu ? (v2i){0x7F7F7F7F, 0x7F7F7F7F} : quant8(v[i], m);
+    if (n < N) *(v2i*)(q + (b * N + n) * K + k0 + 8 * pc) = c;
+    if ((pc & 3) == 0) srow[(kb >> 2) * (kD2N * 4) + (r0 + i) * 4 + (kb & 3)] = (uint8_t)byte;
+  }
+
+  // ---- colwise: amax of each of the lane's 8 columns over the 32-row block
+  us2 cm[4] = {(us2){0, 0}, (us2){0, 0}, (us2){0, 0}, (us2){0, 0}};
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      cm[d] = __builtin_elementwise_max(cm[d], __builtin_bit_cast(us2, (uint32_t)v[i][d] & 0x7FFF7FFFu));
+  uint32_t cbyte[8];
+  float cmul[8];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t mine = __builtin_bit_cast(uint32_t, cm[d]);
+    const uint32_t other = (uint32_t)__shfl_xor((int)mine, 32);
+    const us2 both = __builtin_elementwise_max(cm[d], __builtin_bit_cast(us2, other));
+    cbyte[2 * d] = e8m0_from_absbits(both[0]);
+    cbyte[2 * d + 1] = e8m0_from_absbits(both[1]);
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) cmul[c] = inv_scale_from_e8m0(cbyte[c] == 0xFFu ? 127u : cbyte[c]);
+  // column c (= 2d + hi) of rows r0 .. r0 + 15: 16 codes, one LDS slot
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int d = c >> 1;
+    const bool hi = c & 1;
+    v4i o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 4 * j;
+      const float x0 = hi ? bf16hi((uint32_t)v[i][d]) : bf16lo((uint32_t)v[i][d]);
+      const float x1 = hi ? bf16hi((uint32_t)v[i + 1][d]) : bf16lo((uint32_t)v[i + 1][d]);
+      const float x2 = hi ? bf16hi((uint32_t)v[i + 2][d]) : bf16lo((uint32_t)v[i + 2][d]);
+      const float x3 = hi ? bf16hi((uint32_t)v[i + 3][d]) : bf16lo((uint32_t)v[i + 3][d]);
+      int a = cvt2_e4m3<false>(x0 * cmul[c], x1 * cmul[c], 0);
+      a = cvt2_e4m3<true>(x2 * cmul[c], x3 * cmul[c], a);
+      o[j] = cbyte[c] == 0xFFu ? 0x7F7F7F7F : a;
+    }
+    const int k = 8 * pc + c;
+    *(v4i*)(codes + k * kD2N + 16 * d2_slot(k, 2 * wv + half)) = o;
+    if (half == 0) scol[(wv >> 2) * (kD2 * 4) + k * 4 + (wv & 3)] = (uint8_t)cbyte[c];
+  }
+  __syncthreads();
+
+  // ---- q_t: row k of the code tile is kD2N codes of output row k0 + k
+  {
+    const int slot = tid % kD2Slots;
+    const int64_t n = n0 + 16 * slot;
+#pragma unroll
+    for (int it = 0; it < kD2 * kD2Slots / kD2Threads; ++it) {
+      const int k = tid / kD2Slots + (kD2Threads / kD2Slots) * it;
+      const v4i x = *(const v4i*)(codes + k * kD2N + 16 * d2_slot(k, slot));
+      if (n < ldq) *(v4i*)(q_t + (b * K + k0 + k) * ldq + n) = x;
+    }
+  }
+  // ---- scales, GEMM layout: s [E][K/128][N][4], s_t [E][ldq/128][K][4]
+#pragma unroll
+  for (int u = 0; u < 2 * kD2N / kD2Threads && ROWWISE; ++u) {
+    const int e = u * kD2Threads + tid;
+    const int ch = e / kD2N, r = e % kD2N;
+    if (n0 + r < N)
+      *(uint32_t*)(s + b * (K / 32) * N + ((k0 >> 7) + ch) * N * 4 + (n0 + r) * 4) =
+          *(const uint32_t*)(srow + ch * (kD2N * 4) + r * 4);
+  }
+  if (st_ld == 0) {
+#pragma unroll
+    for (int u = 0; u < (kD2N / 128) * kD2 / kD2Threads; ++u) {
+      const int e = u * kD2Threads + tid;
+      const int ch = e / kD2, r = e % kD2;
+      if (n0 + 128 * ch < ldq)
+        *(uint32_t*)(s_t + b * (ldq / 32) * K + ((n0 >> 7) + ch) * K * 4 + (k0 + r) * 4) =
+            *(const uint32_t*)(scol + ch * (kD2 * 4) + r * 4);
+    }
+  } else {
+    // row-major: thread t owns column k = t / 2 and four of its eight blocks
+    const int k = tid >> 1, g = tid & 1;
+    const uint32_t w4 = *(const uint32_t*)(scol + g * (kD2 * 4) + k * 4);
+    uint8_t* sp = s_t + (b * K + k0 + k) * st_ld + (n0 >> 5) + 4 * g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if ((n0 >> 5) + 4 * g + j < st_ld) sp[j] = (uint8_t)(w4 >> (8 * j));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 32x32: x viewed as [rows, cols] (batch folded into rows; rows % 32 == 0).
 // A workgroup covers 32 rows x 512 columns; wave w covers columns
 // [128w, 128w+128) = four 32x32 tiles.  Lane l holds 8 columns (chunk l%16) of
@@ -421,6 +582,12 @@ hipError_t launch_quant_dual(const uint16_t* w, int64_t E, int64_t N, int64_t K,
                              uint8_t* s, uint8_t* q_t, uint8_t* s_t, hipStream_t st, const int32_t* rows,
                              int64_t src_rows, int topk) {
   if (E == 0 || ldq == 0 || K == 0) return hipSuccess;
+  if (K % kD2 == 0) {
+    dim3 grid((unsigned)(K / kD2), (unsigned)((ldq + kD2N - 1) / kD2N), (unsigned)E);
+    hipLaunchKernelGGL(quant_dual256_kernel<true>, grid, dim3(kD2Threads), 0, st, w, N, K, ldq, q, s, q_t, s_t,
+                       (int64_t)0, rows, rows ? src_rows * topk : N, (uint32_t)(rows ? topk : 1));
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)(K / kColTile), (unsigned)(ldq / kColTile), (unsigned)E);
   hipLaunchKernelGGL(quant_dual_kernel, grid, dim3(256), 0, st, w, N, K, ldq, q, s, q_t, s_t, rows,
                      rows ? src_rows * topk : N, (uint32_t)(rows ? topk : 1));
@@ -441,6 +608,14 @@ hipError_t launch_quant_rowwise_gather(const uint16_t* x, int64_t src_rows, cons
 hipError_t launch_quant_colwise(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q_t,
                                 int64_t ldq, uint8_t* s_t, int64_t lds, int gemm_layout, hipStream_t st) {
   if (batch == 0 || rows == 0 || cols == 0) return hipSuccess;
+  if (cols % kD2 == 0 && (gemm_layout ? ldq % 128 == 0 : ldq == rows)) {
+    // codes of rows [rows, ldq) are zero codes (ldq rounded up to the tile)
+    dim3 grid((unsigned)(cols / kD2), (unsigned)((ldq + kD2N - 1) / kD2N), (unsigned)batch);
+    hipLaunchKernelGGL(quant_dual256_kernel<false>, grid, dim3(kD2Threads), 0, st, x, rows, cols, ldq,
+                       (uint8_t*)nullptr, (uint8_t*)nullptr, q_t, s_t, gemm_layout ? (int64_t)0 : lds,
+                       (const int32_t*)nullptr, rows, 1u);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((cols + kColTile - 1) / kColTile), (unsigned)((rows + kColTile - 1) / kColTile),
             (unsigned)batch);
   hipLaunchKernelGGL(quant_colwise_kernel, grid, dim3(256), 0, st, x, rows, cols, q_t, ldq, s_t, lds, gemm_layout);

@@ -52,6 +52,9 @@ def _check_dual(x_bits: np.ndarray, ldq, tag: str):
     ((416, 384), None, 43, 1.0),     # several tiles, ragged last row tile
     ((256, 128), 512, 44, 1.0),      # explicit wider ldq: two all-padding row tiles
     ((160, 128), None, 45, 300.0),   # saturation path
+    ((288, 512), None, 47, 1.0),     # 256 x 256 tiles: a partial row tile, ldq 384 ends inside a tile
+    ((256, 768), 512, 48, 1.0),      # 256 x 256 tiles: the second row tile is all padding
+    ((160, 256), None, 49, 300.0),   # 256 x 256 tiles, saturation path
 ])
 def test_quantize_dual_matches_oracle(shape, ldq, seed, std):
     require_gpu()
@@ -62,13 +65,15 @@ def test_quantize_dual_matches_oracle(shape, ldq, seed, std):
 
 def test_quantize_dual_all_bf16_patterns():
     """Every bf16 bit pattern (NaN, Inf, zeros, subnormals) in one [512, 128]
-    input with a padded transposed output, in pattern order and shuffled."""
+    and one [256, 256] input (the two tile kernels) with a padded transposed
+    output, in pattern order and shuffled."""
     require_gpu()
     pats = inp.all_bf16_patterns()
     rng = np.random.default_rng(46)
     for tag, arr in (("ordered", pats), ("shuffled", rng.permutation(pats))):
         log(f"quantize_dual all bf16 patterns {tag}")
         _check_dual(arr.reshape(512, 128), 640, tag)
+        _check_dual(arr.reshape(256, 256), 384, tag + " 256-column tiles")
 
 
 def test_quantize_dual_rejects_bad_shapes():

@@ -48,6 +48,7 @@ MODES = ["rowwise", "colwise", "32x32"]
     ((160, 384), 4, 300.0),         # large magnitudes, saturation path
     ((32, 32), 5, 1.0),             # a single block / tile
     ((224, 200), 6, 1.0),           # ragged column count (not a tile multiple)
+    ((2, 288, 512), 7, 0.02),       # batched, 256-column tiles with a partial last row tile
 ])
 def test_quant_seeded(mode, shape, seed, std):
     require_gpu()

@@ -42,6 +42,7 @@ def _check_weights(W_bits: np.ndarray, tag: str):
     ((2, 128, 128), 31, 0.02),      # one tile per expert
     ((3, 256, 384), 32, 0.02),      # several tiles, rectangular
     ((1, 384, 256), 33, 300.0),     # saturation path
+    ((2, 512, 512), 34, 0.02),      # 256 x 256 tiles, two per expert and orientation
 ])
 def test_quantize_weights_matches_oracle(shape, seed, std):
     require_gpu()
