@@ -283,6 +283,20 @@ mx_status mx_grouped_gemm_mx_rows(const uint8_t* X, const uint8_t* sX, const uin
                                   int scale_layout, const int32_t* offs, int64_t I, int64_t J, int64_t Kc, int64_t E,
                                   const int32_t* row_map, uint16_t* C, int64_t c_rows, void* stream);
 
+/* mx_grouped_gemm_mx_rows with fp32 output C [c_rows, J] (accumulators stored
+ * unrounded): the per-item input gradients of a top-k router, before
+ * mx_topk_sum_rows adds each token's k of them. */
+mx_status mx_grouped_gemm_mx_rows_f32(const uint8_t* X, const uint8_t* sX, const uint8_t* Y, const uint8_t* sY,
+                                      int scale_layout, const int32_t* offs, int64_t I, int64_t J, int64_t Kc,
+                                      int64_t E, const int32_t* row_map, float* C, int64_t c_rows, void* stream);
+
+/* Gradient of the top-k token gather: a token feeds its k items, so its input
+ * gradient is the sum of theirs.  out[t, c] = bf16(x[t*k, c] + x[t*k+1, c]
+ * + ... + x[t*k+k-1, c]), summed in fp32 in slot order and rounded to nearest
+ * even once.  x fp32 [T*k, cols], out bf16 [T, cols], both 16-byte aligned;
+ * 1 <= k <= 1024, cols % 8 == 0. */
+mx_status mx_topk_sum_rows(const float* x, int64_t T, int64_t k, int64_t cols, uint16_t* out, void* stream);
+
 /* ------------------------------------------------------------------------
  * Prequantized expert weights: the weight 4-tuple of the MoK expert PR
  * review (weight_fp8 / weight_scale feed the forward, weight_t_fp8 /

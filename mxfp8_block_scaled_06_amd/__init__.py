@@ -24,6 +24,7 @@ __all__ = [
     "OP_FWD", "OP_DGRAD", "OP_WGRAD", "OP_FWD_Q", "OP_DGRAD_Q", "SCALES_ROWMAJOR", "SCALES_GEMM",
     "mx_check_offsets", "check_offsets", "mx_grouped_mm_fwd_q_noalloc", "NOALLOC_SCRATCH_BYTES",
     "mx_route", "route_capacity", "mx_quantize_dual_gather", "mx_grouped_gemm_mx_rows", "mx_routed_experts",
+    "mx_topk_sum_rows",
 ]
 
 OP_FWD, OP_DGRAD, OP_WGRAD, OP_FWD_Q, OP_DGRAD_Q = 0, 1, 2, 3, 4
@@ -72,6 +73,10 @@ def load_library():
     lib.mx_grouped_gemm_mx_rows.restype = c_int
     lib.mx_grouped_gemm_mx_rows.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp,
                                             c_vp, c_i64, c_vp]
+    lib.mx_grouped_gemm_mx_rows_f32.restype = c_int
+    lib.mx_grouped_gemm_mx_rows_f32.argtypes = lib.mx_grouped_gemm_mx_rows.argtypes
+    lib.mx_topk_sum_rows.restype = c_int
+    lib.mx_topk_sum_rows.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]
     lib.mx_route.restype = c_int
     lib.mx_route.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]
     lib.mx_quantize_dual_gather.restype = c_int
@@ -268,14 +273,20 @@ def _gemm_operands(X, sX, Y, sY, offs, mode, scale_layout):
     return I, J, Kc, E, SCALES_GEMM if scale_layout == "gemm" else SCALES_ROWMAJOR
 
 
-def mx_grouped_gemm_mx_rows(X, sX, Y, sY, offs, row_map, c_rows: Optional[int] = None, out=None):
-    """mx_grouped_gemm_mx (mode 0, bf16) storing grouped row i to out row
+def mx_grouped_gemm_mx_rows(X, sX, Y, sY, offs, row_map, c_rows: Optional[int] = None, out=None,
+                            out_dtype=None):
+    """mx_grouped_gemm_mx (mode 0) storing grouped row i to out row
     row_map[i] (rows whose entry lies outside [0, c_rows) are dropped; out
     rows no entry names are left as they were).  row_map int32 [I] on the GPU
-    (the `rows` of mx_route); out bf16 [c_rows, J] (default c_rows: out's
-    rows, else I; a new out starts at zero)."""
+    (the `rows` of mx_route); out bf16 (or fp32 with out_dtype=torch.float32)
+    [c_rows, J] (default c_rows: out's rows, else I; a new out starts at
+    zero)."""
     import torch
     lib = load_library()
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.bfloat16
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
     I, J, Kc, E, layout = _gemm_operands(X, sX, Y, sY, offs, 0, "gemm")
     _require(row_map, torch.int32, "row_map")
     if tuple(row_map.shape) != (I,):
@@ -283,11 +294,25 @@ def mx_grouped_gemm_mx_rows(X, sX, Y, sY, offs, row_map, c_rows: Optional[int] =
     if c_rows is None:
         c_rows = out.shape[0] if out is not None else I
     if out is None:
-        out = torch.zeros((c_rows, J), dtype=torch.bfloat16, device=X.device)
-    out = _out(out, (c_rows, J), torch.bfloat16, X.device, "out")
-    _check("mx_grouped_gemm_mx_rows",
-           lib.mx_grouped_gemm_mx_rows(_ptr(X), _ptr(sX), _ptr(Y), _ptr(sY), layout, _ptr(offs), I, J, Kc, E,
-                                       _ptr(row_map), _ptr(out), int(c_rows), _stream(X.device)))
+        out = torch.zeros((c_rows, J), dtype=out_dtype, device=X.device)
+    out = _out(out, (c_rows, J), out_dtype, X.device, "out")
+    name = "mx_grouped_gemm_mx_rows" if out_dtype == torch.bfloat16 else "mx_grouped_gemm_mx_rows_f32"
+    _check(name, getattr(lib, name)(_ptr(X), _ptr(sX), _ptr(Y), _ptr(sY), layout, _ptr(offs), I, J, Kc, E,
+                                    _ptr(row_map), _ptr(out), int(c_rows), _stream(X.device)))
+    return out
+
+
+def mx_topk_sum_rows(x, k: int, out=None):
+    """x fp32 [T*k, cols] -> bf16 [T, cols]: each token's k rows summed in fp32
+    in slot order, rounded to nearest even once (the top-k gather's gradient)."""
+    import torch
+    lib = load_library()
+    _require(x, torch.float32, "x")
+    if x.dim() != 2 or x.shape[0] % k:
+        raise ValueError(f"x must be [T*k, cols] with k={k}, got {tuple(x.shape)}")
+    T, cols = x.shape[0] // k, x.shape[1]
+    out = _out(out, (T, cols), torch.bfloat16, x.device, "out")
+    _check("mx_topk_sum_rows", lib.mx_topk_sum_rows(_ptr(x), T, int(k), cols, _ptr(out), _stream(x.device)))
     return out
 
 
@@ -618,8 +643,10 @@ def mx_quantize_dual_gather(x, rows, topk: int = 1, ldq: Optional[int] = None, q
 
 
 def mx_routed_experts(x, expert_idx, W, check: bool = True, weights=None, cache=None):
-    """Differentiable routed experts: out[t] = x[t] @ W[expert_idx[t]]^T, with
-    the grouping, the token gather (inside the quantizer) and the scatter
-    back to token order (inside the GEMM epilogue) on the device."""
+    """Differentiable routed experts: out[t] = x[t] @ W[expert_idx[t]]^T for a
+    top-1 router (expert_idx [T]), out[t, j] = x[t] @ W[expert_idx[t, j]]^T for
+    a top-k router (expert_idx [T, k]), with the grouping, the token gather
+    (inside the quantizer) and the scatter back to item order (inside the GEMM
+    epilogue) on the device."""
     from .autograd import mx_routed_experts as _f
     return _f(x, expert_idx, W, check, weights, cache)

@@ -34,7 +34,7 @@ import weakref
 
 from . import (mx_grouped_gemm_mx, mx_grouped_gemm_mx_rows, mx_grouped_mm_dgrad_q, mx_grouped_mm_fwd_q,
                mx_quantize_dual, mx_quantize_dual_gather, mx_quantize_rowwise_gather, mx_quantize_weights,
-               mx_route)
+               mx_route, mx_topk_sum_rows)
 
 
 class WeightCache:
@@ -210,24 +210,27 @@ class _MXRouted:
 
             class Fn(torch.autograd.Function):
                 @staticmethod
-                def forward(ctx, x, W, offs, rows, mx4, zero_fill):
+                def forward(ctx, x, W, offs, rows, mx4, zero_fill, topk):
                     qW, sW, qWt, sWt = mx4
-                    T = x.shape[0]
+                    n_items = x.shape[0] * topk
                     cap = rows.shape[0]
                     alloc = torch.zeros if zero_fill else torch.empty
-                    out = alloc((T, W.shape[1]), dtype=torch.bfloat16, device=x.device)
-                    if ctx.needs_input_grad[1]:
-                        # tokens gathered into their expert groups inside the
-                        # quantizer, in both orientations (wgrad keeps the
-                        # 32x1-along-tokens codes)
-                        qA, sA, qAt, sAt = mx_quantize_dual_gather(x, rows, ldq=cap)
+                    out = alloc((n_items, W.shape[1]), dtype=torch.bfloat16, device=x.device)
+                    if ctx.needs_input_grad[1] or topk > 1:
+                        # items gathered into their expert groups inside the
+                        # quantizer (item a reads token a // topk), in both
+                        # orientations (wgrad keeps the 32x1-along-items codes)
+                        qA, sA, qAt, sAt = mx_quantize_dual_gather(x, rows, topk=topk, ldq=cap)
+                        if not ctx.needs_input_grad[1]:
+                            qAt = sAt = None
                     else:
                         qA, sA = mx_quantize_rowwise_gather(x, rows)
                         qAt = sAt = None
-                    # the epilogue stores each grouped row at its token's row
+                    # the epilogue stores each grouped row at its item's row
                     mx_grouped_gemm_mx_rows(qA, sA, qW, sW, offs, rows, out=out)
                     del qA, sA, qW, sW
                     ctx.zero_fill = zero_fill
+                    ctx.topk = topk
                     ctx.save_for_backward(offs, rows, qWt, sWt, qAt, sAt)
                     return out
 
@@ -235,6 +238,7 @@ class _MXRouted:
                 def backward(ctx, dOut):
                     offs, rows, qWt, sWt, qAt, sAt = ctx.saved_tensors
                     dOut = dOut.contiguous()
+                    topk = ctx.topk
                     dx = dW = None
                     alloc = torch.zeros if ctx.zero_fill else torch.empty
                     if ctx.needs_input_grad[1]:
@@ -243,41 +247,57 @@ class _MXRouted:
                     elif ctx.needs_input_grad[0]:
                         qG, sG = mx_quantize_rowwise_gather(dOut, rows)
                     if ctx.needs_input_grad[0]:
-                        dx = alloc((dOut.shape[0], qWt.shape[1]), dtype=torch.bfloat16, device=dOut.device)
-                        mx_grouped_gemm_mx_rows(qG, sG, qWt, sWt, offs, rows, out=dx)
-                    return dx, dW, None, None, None, None
+                        K = qWt.shape[1]
+                        if topk == 1:
+                            dx = alloc((dOut.shape[0], K), dtype=torch.bfloat16, device=dOut.device)
+                            mx_grouped_gemm_mx_rows(qG, sG, qWt, sWt, offs, rows, out=dx)
+                        else:
+                            # per-item gradients in fp32, then each token's
+                            # topk of them summed and rounded once (the adjoint
+                            # of the gather that fed the items)
+                            items = torch.zeros((dOut.shape[0], K), dtype=torch.float32, device=dOut.device)
+                            mx_grouped_gemm_mx_rows(qG, sG, qWt, sWt, offs, rows, out=items)
+                            dx = mx_topk_sum_rows(items, topk)
+                    return dx, dW, None, None, None, None, None
 
             cls.fn = Fn
         return cls.fn
 
 
 def mx_routed_experts(x, expert_idx, W, check: bool = True, weights=None, cache: WeightCache | None = None):
-    """Differentiable top-1 routed experts: out[t] = x[t] @ W[expert_idx[t]]^T.
+    """Differentiable routed experts: out[t, j] = x[t] @ W[expert_idx[t, j]]^T.
 
-    x bf16 [T, K] in token order; expert_idx int32 [T] on the device (the
-    router's choice per token); W bf16 [E, N, K] with N % 128 == 0 and
-    K % 128 == 0; out bf16 [T, N] in token order.  mx_route groups the tokens
-    by expert on the device (each expert's tokens in their original order,
-    padded with zero rows to a multiple of 32), the quantizer gathers the
-    tokens into that grouping, and the GEMM epilogue stores every row back at
-    its token, so neither a permuted copy of the tokens nor an unpermute pass
-    exists; the backward gathers dOut the same way.  Weights as for
+    x bf16 [T, K] in token order; expert_idx int32 on the device, [T] for a
+    top-1 router (out bf16 [T, N]) or [T, k] for a top-k router (out bf16
+    [T, k, N], one row per token-expert pair; the caller's combine weights and
+    sums them); W bf16 [E, N, K] with N % 128 == 0 and K % 128 == 0.
+    mx_route groups the items (token-expert pairs, token-major) by expert on
+    the device (each expert's items in their original order, padded with zero
+    rows to a multiple of 32), the quantizer gathers the tokens into that
+    grouping, and the GEMM epilogue stores every row back at its item, so
+    neither a permuted copy of the tokens nor an unpermute pass exists; the
+    backward gathers dOut the same way.  For k > 1 the input gradient of a
+    token sums its k items' fp32 gradients and rounds once.  Weights as for
     mx_grouped_mm (`weights`, else the cache).
 
     check=True reads the routing status (one synchronization) and raises on
-    an expert id outside [0, E).  With check=False such tokens are dropped:
-    their output rows and input gradients are zero."""
+    an expert id outside [0, E).  With check=False such items are dropped:
+    their output rows are zero and they add nothing to the gradients."""
     import torch
     if x.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
         raise TypeError("mx_routed_experts: x and W must be bfloat16")
-    if expert_idx.dtype != torch.int32 or expert_idx.dim() != 1 or expert_idx.shape[0] != x.shape[0]:
-        raise ValueError(f"mx_routed_experts: expert_idx must be int32 [T={x.shape[0]}] (one expert per token)")
     if x.dim() != 2 or W.dim() != 3 or W.shape[2] != x.shape[1]:
         raise ValueError("mx_routed_experts: x must be [T, K] and W [E, N, K]")
+    T = x.shape[0]
+    if expert_idx.dtype != torch.int32 or expert_idx.dim() not in (1, 2) or expert_idx.shape[0] != T:
+        raise ValueError(f"mx_routed_experts: expert_idx must be int32 [T={T}] or [T={T}, k]")
+    topk = 1 if expert_idx.dim() == 1 else expert_idx.shape[1]
+    if topk < 1:
+        raise ValueError("mx_routed_experts: k must be at least 1")
     E, N, K = W.shape
     if K % 128 or N % 128:
         raise ValueError(f"mx_routed_experts: N={N} and K={K} must be multiples of 128")
-    offs, rows, _pos, status = mx_route(expert_idx.contiguous(), E)
+    offs, rows, _pos, status = mx_route(expert_idx.contiguous().reshape(-1), E)
     if check:
         if int(status.item()):
             raise ValueError(f"mx_routed_experts: an expert id lies outside [0, {E})")
@@ -287,4 +307,5 @@ def mx_routed_experts(x, expert_idx, W, check: bool = True, weights=None, cache:
         mx4 = tuple(weights)
     else:
         mx4 = (cache if cache is not None else _DEFAULT_CACHE).get(W)
-    return _MXRouted.get().apply(x.contiguous(), W, offs, rows, mx4, not check)
+    out = _MXRouted.get().apply(x.contiguous(), W, offs, rows, mx4, not check, topk)
+    return out if expert_idx.dim() == 1 else out.view(T, topk, N)

@@ -219,6 +219,17 @@ mx_status grouped_gemm_impl(const char* fn, const uint8_t* X, const uint8_t* sX,
   return hip_status(mxk::launch_grouped_gemm(a, (hipStream_t)stream), fn);
 }
 
+mx_status gemm_rows_impl(const char* fn, const uint8_t* X, const uint8_t* sX, const uint8_t* Y, const uint8_t* sY,
+                         int scale_layout, const int32_t* offs, int64_t I, int64_t J, int64_t Kc, int64_t E,
+                         const int32_t* row_map, void* C, int64_t c_rows, int out_f32, void* stream) {
+  if (c_rows < 0 || c_rows >= ((int64_t)1 << 31))
+    return fail(MX_ERR_SHAPE, "%s: c_rows=%lld outside [0, 2^31)", fn, (long long)c_rows);
+  if (c_rows == 0) return MX_OK;
+  if (!row_map) return fail(MX_ERR_NULL, "%s: null row map", fn);
+  if (!aligned(row_map, 4)) return fail(MX_ERR_ALIGN, "%s: row_map must be 4-byte aligned", fn);
+  return grouped_gemm_impl(fn, X, sX, Y, sY, scale_layout, offs, 0, I, J, Kc, E, C, out_f32, stream, row_map, c_rows);
+}
+
 }  // namespace
 
 extern "C" {
@@ -236,16 +247,32 @@ mx_status mx_grouped_gemm_mx_f32(const uint8_t* X, const uint8_t* sX, const uint
                            stream);
 }
 
+
 mx_status mx_grouped_gemm_mx_rows(const uint8_t* X, const uint8_t* sX, const uint8_t* Y, const uint8_t* sY,
                                   int scale_layout, const int32_t* offs, int64_t I, int64_t J, int64_t Kc, int64_t E,
                                   const int32_t* row_map, uint16_t* C, int64_t c_rows, void* stream) {
-  const char* fn = "mx_grouped_gemm_mx_rows";
-  if (c_rows < 0 || c_rows >= ((int64_t)1 << 31))
-    return fail(MX_ERR_SHAPE, "%s: c_rows=%lld outside [0, 2^31)", fn, (long long)c_rows);
-  if (c_rows == 0) return MX_OK;
-  if (!row_map) return fail(MX_ERR_NULL, "%s: null row map", fn);
-  if (!aligned(row_map, 4)) return fail(MX_ERR_ALIGN, "%s: row_map must be 4-byte aligned", fn);
-  return grouped_gemm_impl(fn, X, sX, Y, sY, scale_layout, offs, 0, I, J, Kc, E, C, 0, stream, row_map, c_rows);
+  return gemm_rows_impl("mx_grouped_gemm_mx_rows", X, sX, Y, sY, scale_layout, offs, I, J, Kc, E, row_map, C, c_rows,
+                        0, stream);
+}
+
+mx_status mx_grouped_gemm_mx_rows_f32(const uint8_t* X, const uint8_t* sX, const uint8_t* Y, const uint8_t* sY,
+                                      int scale_layout, const int32_t* offs, int64_t I, int64_t J, int64_t Kc,
+                                      int64_t E, const int32_t* row_map, float* C, int64_t c_rows, void* stream) {
+  return gemm_rows_impl("mx_grouped_gemm_mx_rows_f32", X, sX, Y, sY, scale_layout, offs, I, J, Kc, E, row_map, C,
+                        c_rows, 1, stream);
+}
+
+mx_status mx_topk_sum_rows(const float* x, int64_t T, int64_t k, int64_t cols, uint16_t* out, void* stream) {
+  const char* fn = "mx_topk_sum_rows";
+  if (T < 0 || cols < 0 || k < 1 || k > 1024)
+    return fail(MX_ERR_SHAPE, "%s: T=%lld k=%lld cols=%lld (k in [1, 1024])", fn, (long long)T, (long long)k,
+                (long long)cols);
+  if (cols % 8 != 0) return fail(MX_ERR_SHAPE, "%s: cols=%lld is not a multiple of 8", fn, (long long)cols);
+  if (T == 0 || cols == 0) return MX_OK;
+  if (T * (cols / 8) >= ((int64_t)1 << 40)) return fail(MX_ERR_SHAPE, "%s: too large", fn);
+  if (!x || !out) return fail(MX_ERR_NULL, "%s: null pointer", fn);
+  if (!aligned(x, 16) || !aligned(out, 16)) return fail(MX_ERR_ALIGN, "%s: x and out must be 16-byte aligned", fn);
+  return hip_status(mxk::launch_topk_sum(x, T, (int)k, cols, out, (hipStream_t)stream), fn);
 }
 
 mx_status mx_route(const int32_t* expert_idx, int64_t n, int64_t E, int64_t cap, int32_t* offs, int32_t* rows,

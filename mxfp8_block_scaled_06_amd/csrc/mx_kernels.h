@@ -55,6 +55,8 @@ hipError_t launch_scales_to_gemm(const uint8_t* s, int64_t batch, int64_t rows, 
 hipError_t launch_quant_32x32(const uint16_t* x, int64_t rows_total, int64_t cols, uint8_t* q, uint8_t* s,
                               hipStream_t st);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t st);
+// out[t] = bf16(sum of the k fp32 rows x[t*k .. t*k+k-1]) (see mx_topk_sum_rows).
+hipError_t launch_topk_sum(const float* x, int64_t T, int k, int64_t cols, uint16_t* out, hipStream_t st);
 // Routing metadata (see mx_route).
 hipError_t launch_route(const int32_t* expert_idx, int64_t T, int64_t E, int64_t cap, int32_t* offs,
                              int32_t* rows, int32_t* pos, int32_t* status, hipStream_t st);

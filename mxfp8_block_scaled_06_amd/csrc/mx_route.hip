@@ -157,6 +157,40 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
   if (tid == 0) status[0] = bad;
 }
 
+// ---------------------------------------------------------------------------
+// Gradient of the top-k gather: a token's input gradient is the sum of the
+// gradients of its k items.  out[t, c] = bf16(sum_{j < k} x[t*k + j, c]) with
+// the sum taken in fp32 in slot order and rounded to nearest even once.  One
+// thread per 8 columns of one token: k 32-byte loads, one 16-byte store.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void topk_sum_kernel(const float* __restrict__ x, int64_t T, int k, int64_t cols,
+                                                       uint16_t* __restrict__ out) {
+  const int64_t per_row = cols >> 3;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= T * per_row) return;
+  const int64_t t = idx / per_row, c = (idx - t * per_row) * 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const v4i* src = (const v4i*)(x + (t * k + j) * cols + c);
+    const v4i a = __builtin_nontemporal_load(src), b = __builtin_nontemporal_load(src + 1);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc[u] += __int_as_float(a[u]);
+      acc[4 + u] += __int_as_float(b[u]);
+    }
+  }
+  const v4i o = {(int)pack_bf16x2_rne(acc[0], acc[1]), (int)pack_bf16x2_rne(acc[2], acc[3]),
+                 (int)pack_bf16x2_rne(acc[4], acc[5]), (int)pack_bf16x2_rne(acc[6], acc[7])};
+  *(v4i*)(out + t * cols + c) = o;
+}
+
+hipError_t launch_topk_sum(const float* x, int64_t T, int k, int64_t cols, uint16_t* out, hipStream_t st) {
+  const int64_t n = T * (cols / 8);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, x, T, k, cols, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const int32_t* expert_idx, int64_t T, int64_t E, int64_t cap, int32_t* offs,
                              int32_t* rows, int32_t* pos, int32_t* status, hipStream_t st) {
   hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, st, expert_idx, (int)T, (int)E, (int)cap,

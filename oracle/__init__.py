@@ -11,5 +11,5 @@ from .mxfp8 import (  # noqa: F401
 )
 from .compare import r1_check, rne_bf16, ulp_bf16  # noqa: F401
 from .route import (  # noqa: F401
-    route_groups, gather_rows, scatter_rows, routed_fwd, routed_dgrad, routed_wgrad,
+    route_groups, gather_rows, scatter_rows, routed_fwd, routed_dgrad, routed_wgrad, topk_sum_rows,
 )

@@ -77,25 +77,44 @@ def scatter_rows(g, rows, n: int):
     return out
 
 
-def routed_fwd(x_bits, expert_idx, W_bits, cap: int, absolute: bool = False):
-    """out[t] = MX(x)[t] @ MX(W[e_t])^T for top-1 routed tokens, in token order."""
+def routed_fwd(x_bits, expert_idx, W_bits, cap: int, absolute: bool = False, topk: int = 1):
+    """out[a] = MX(x)[a // topk] @ MX(W[e_a])^T for every routed item a (a
+    token of a top-1 router, or item a = token * topk + slot), in item order."""
     E = W_bits.shape[0]
     offs, rows, _, _ = route_groups(expert_idx, E, cap)
-    g = grouped_mm_fwd(gather_rows(x_bits, rows), W_bits, offs, absolute=absolute)
-    return scatter_rows(g, rows, x_bits.shape[0])
+    g = grouped_mm_fwd(gather_rows(x_bits, rows, topk), W_bits, offs, absolute=absolute)
+    return scatter_rows(g, rows, len(expert_idx))
 
 
-def routed_dgrad(dOut_bits, expert_idx, W_bits, cap: int, absolute: bool = False):
-    """dx[t] = MX(dOut)[t] @ MX_t(W[e_t]) in token order (W blocked along N)."""
+def routed_dgrad(dOut_bits, expert_idx, W_bits, cap: int, absolute: bool = False, topk: int = 1):
+    """dx[t] = sum over the token's items a of MX(dOut)[a] @ MX_t(W[e_a])
+    (W blocked along N), in token order; dOut is in item order.  The sum of a
+    token's items is the adjoint of the gather that fed them (reading R-topk),
+    taken here exactly in fp64."""
     E = W_bits.shape[0]
     offs, rows, _, _ = route_groups(expert_idx, E, cap)
     g = grouped_mm_dgrad(gather_rows(dOut_bits, rows), W_bits, offs, absolute=absolute)
-    return scatter_rows(g, rows, dOut_bits.shape[0])
+    items = scatter_rows(g, rows, dOut_bits.shape[0])
+    return items.reshape(-1, topk, items.shape[1]).sum(axis=1)
 
 
-def routed_wgrad(dOut_bits, x_bits, expert_idx, E: int, cap: int, absolute: bool = False):
-    """dW[e] = sum over expert e's tokens of dOut[t]^T x[t], both operands
-    quantized in 32-row blocks along the padded grouping (reading R-pad)."""
+def routed_wgrad(dOut_bits, x_bits, expert_idx, E: int, cap: int, absolute: bool = False, topk: int = 1):
+    """dW[e] = sum over expert e's items a of dOut[a]^T x[a // topk], both
+    operands quantized in 32-row blocks along the padded grouping (R-pad)."""
     offs, rows, _, _ = route_groups(expert_idx, E, cap)
     used = rows[:int(offs[-1])]               # the groups; rows past them are zeros in no group
-    return grouped_mm_wgrad(gather_rows(dOut_bits, used), gather_rows(x_bits, used), offs, absolute=absolute)
+    return grouped_mm_wgrad(gather_rows(dOut_bits, used), gather_rows(x_bits, used, topk), offs, absolute=absolute)
+
+
+def topk_sum_rows(x_f32, topk: int):
+    """bf16 bits of each token's sum of its topk fp32 rows: fp32 additions in
+    slot order starting from +0, then one round to nearest even (the reading
+    of the gradient sum for a kernel that keeps fp32 accumulators)."""
+    x = np.asarray(x_f32, dtype=np.float32)
+    acc = np.zeros((x.shape[0] // topk,) + x.shape[1:], dtype=np.float32)
+    for j in range(topk):
+        acc = acc + x[j::topk]
+    # round to nearest even on the 16 dropped bits (finite values): add half an
+    # ulp less one, plus the kept lsb, and truncate
+    u = acc.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)

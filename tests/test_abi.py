@@ -221,6 +221,21 @@ def test_routing_entry_points_validate():
     assert m(FAKE, FAKE, FAKE, FAKE, mx.SCALES_ROWMAJOR, FAKE, 256, 128, 128, 2, FAKE, FAKE, 10, None) == 6
 
 
+def test_topk_entry_points_validate():
+    lib = _lib()
+    t = lib.mx_topk_sum_rows
+    assert t(FAKE, 10, 0, 64, FAKE, None) == 2           # k < 1
+    assert t(FAKE, 10, 1025, 64, FAKE, None) == 2        # k > 1024
+    assert t(FAKE, 10, 2, 60, FAKE, None) == 2           # cols % 8
+    assert t(None, 10, 2, 64, FAKE, None) == 1           # null input
+    assert t(FAKE + 4, 10, 2, 64, FAKE, None) == 3       # misaligned input
+    assert t(None, 0, 2, 64, None, None) == 0            # nothing to do
+    m = lib.mx_grouped_gemm_mx_rows_f32
+    args = (FAKE, FAKE, FAKE, FAKE, mx.SCALES_GEMM, FAKE, 256, 128, 128, 2)
+    assert m(*args, FAKE, FAKE, -1, None) == 2
+    assert m(*args, None, FAKE, 10, None) == 1
+
+
 def test_noalloc_forward_refuses_sizes_past_its_scratch():
     """The allocation-free forward checks its static scratch limit before any
     device call: too many activations give MX_ERR_WORKSPACE and a clear text."""

@@ -297,3 +297,83 @@ def test_routed_experts_full_size_llama4_sampled():
     rep = oracle.r1_check(got[picks], r, abs_terms=a)
     log(f"  sampled rows: normwise={rep['normwise_rel']:.2e}")
     assert rep["ok"], rep
+
+
+# --------------------------------------------------------------------------
+# Top-k routers
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("T,k,cols", [(300, 3, 264), (64, 1, 128), (1000, 8, 512)])
+def test_topk_sum_rows_matches_oracle(T, k, cols):
+    torch = require_gpu()
+    import mxfp8_block_scaled_06_amd as mx
+    rng = np.random.default_rng(70 + k)
+    x = (rng.standard_normal((T * k, cols)) * np.exp2(rng.integers(-20, 20, size=(T * k, 1)))).astype(np.float32)
+    log(f"topk sum T={T} k={k} cols={cols}")
+    got = mx.mx_topk_sum_rows(torch.from_numpy(x).cuda(), k)
+    assert np.array_equal(bf16_host_bits(got), oracle.topk_sum_rows(x, k))
+
+
+def test_rows_gemm_f32_equals_gemm_f32_then_scatter():
+    torch = require_gpu()
+    import mxfp8_block_scaled_06_amd as mx
+    rng = np.random.default_rng(71)
+    T, k, E, K, N = 200, 2, 3, 256, 128
+    ids = rng.integers(0, E, size=T * k).astype(np.int32)
+    x = inp.random_bf16((T, K), seed=72, outliers=True)
+    W = inp.random_bf16((E, N, K), seed=73, std=0.02)
+    log("rows GEMM fp32 output")
+    offs, rows, _, _ = mx.mx_route(to_dev_i32(ids), E)
+    qX, sX, _, _ = mx.mx_quantize_dual_gather(to_dev_bf16(x), rows, topk=k)
+    qW, sW, _, _ = mx.mx_quantize_weights(to_dev_bf16(W))
+    plain = mx.mx_grouped_gemm_mx_f32(qX, sX, qW, sW, offs, 0)
+    got = mx.mx_grouped_gemm_mx_rows(qX, sX, qW, sW, offs, rows, c_rows=T * k, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows_h = rows.cpu().numpy()
+    live = np.flatnonzero(rows_h >= 0)
+    want = np.zeros((T * k, N), dtype=np.float32)
+    want[rows_h[live]] = plain.cpu().numpy()[live]
+    assert np.array_equal(got.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("k,counts_seed", [(2, 80), (4, 81)])
+def test_routed_experts_topk_autograd(k, counts_seed):
+    torch = require_gpu()
+    import mxfp8_block_scaled_06_amd as mx
+    T, E, K, N = 160, 5, 256, 256
+    rng = np.random.default_rng(counts_seed)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    ids[ids == 3] = 1                                   # expert 3 gets no items
+    x = inp.random_bf16((T, K), seed=counts_seed + 1, outliers=True)
+    W = inp.random_bf16((E, N, K), seed=counts_seed + 2, std=0.02)
+    G = inp.random_bf16((T * k, N), seed=counts_seed + 3, std=1e-3)
+    log(f"routed experts top-{k} autograd T={T} E={E}")
+    xd = to_dev_bf16(x).requires_grad_(True)
+    Wd = to_dev_bf16(W).requires_grad_(True)
+    out = mx.mx_routed_experts(xd, to_dev_i32(ids), Wd, cache=WeightCache())
+    assert tuple(out.shape) == (T, k, N)
+    out.backward(to_dev_bf16(G).view(T, k, N))
+    torch.cuda.synchronize()
+    flat = ids.reshape(-1)
+    cap = mx.route_capacity(T * k, E)
+    for name, got, ref, absr in (
+            ("out", bf16_host_bits(out).reshape(T * k, N), oracle.routed_fwd(x, flat, W, cap, topk=k),
+             oracle.routed_fwd(x, flat, W, cap, absolute=True, topk=k)),
+            ("dx", bf16_host_bits(xd.grad), oracle.routed_dgrad(G, flat, W, cap, topk=k),
+             oracle.routed_dgrad(G, flat, W, cap, absolute=True, topk=k)),
+            ("dW", bf16_host_bits(Wd.grad), oracle.routed_wgrad(G, x, flat, E, cap, topk=k),
+             oracle.routed_wgrad(G, x, flat, E, cap, absolute=True, topk=k))):
+        rep = oracle.r1_check(got, ref, abs_terms=absr)
+        log(f"  {name}: normwise={rep['normwise_rel']:.2e} plain_frac={rep['plain_r1_frac']:.2e}")
+        assert rep["ok"], (name, rep)
+    assert (bf16_host_bits(Wd.grad)[3] == 0).all()
+    # fp64 autograd of the unquantized top-k layer
+    x64 = torch.from_numpy(oracle.bf16_to_f64(x)).requires_grad_(True)
+    W64 = torch.from_numpy(oracle.bf16_to_f64(W)).requires_grad_(True)
+    ref = torch.stack([x64[t // k] @ W64[int(flat[t])].T for t in range(T * k)])
+    ref.backward(torch.from_numpy(oracle.bf16_to_f64(G)))
+    for name, got, r64, mxref in (
+            ("out", bf16_host_bits(out).reshape(T * k, N), ref.detach().numpy(),
+             oracle.routed_fwd(x, flat, W, cap, topk=k)),
+            ("dx", bf16_host_bits(xd.grad), x64.grad.numpy(), oracle.routed_dgrad(G, flat, W, cap, topk=k)),
+            ("dW", bf16_host_bits(Wd.grad), W64.grad.numpy(), oracle.routed_wgrad(G, x, flat, E, cap, topk=k))):
+        assert _normwise(oracle.bf16_to_f64(got), r64) <= 2 * _normwise(mxref, r64) + 4e-3, name

@@ -172,3 +172,60 @@ def test_gather_rows_topk_takes_the_token_of_each_item():
     rows = np.array([5, -1, 0, 7, 8], dtype=np.int32)     # items of a top-2 router
     g = oracle.gather_rows(x, rows, topk=2)
     assert g.tolist() == [x[2].tolist(), [0, 0, 0], x[0].tolist(), x[3].tolist(), [0, 0, 0]]
+
+
+# --------------------------------------------------------------------------
+# Top-k routers: item a = token * k + slot
+# --------------------------------------------------------------------------
+def test_topk_sum_rows_rounds_once_to_nearest_even():
+    # 1 + 2^-8 lies halfway between bf16 1.0 and 1 + 2^-7: ties go to the even 1.0;
+    # 1 + 3 * 2^-8 lies halfway between 1 + 2^-7 (odd) and 1 + 2^-6 (even)
+    x = np.array([[1.0, 1.0], [2.0 ** -8, 3 * 2.0 ** -8], [3.0, -0.0], [1.0, 2.0]], dtype=np.float32)
+    got = oracle.topk_sum_rows(x, 2)
+    assert got.tolist() == [[0x3F80, 0x3F82], [0x4080, 0x4000]]
+    # one slot: a plain fp32 -> bf16 rounding, +0 for -0 (the sum starts at +0)
+    assert oracle.topk_sum_rows(np.array([[-0.0, 1.0 + 2.0 ** -7]], np.float32), 1).tolist() == [[0x0000, 0x3F81]]
+
+
+def _topk_case(T, k, E, K, N, seed):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, E, size=T * k)
+    x = inp.random_bf16((T, K), seed=seed + 1, outliers=True)
+    W = inp.random_bf16((E, N, K), seed=seed + 2, std=0.02)
+    G = inp.random_bf16((T * k, N), seed=seed + 3, std=1e-3)
+    return ids, x, W, G, T * k + 31 * E
+
+
+def test_topk_routed_fwd_and_dgrad_equal_the_per_item_definition():
+    T, k, E = 40, 3, 4
+    ids, x, W, G, cap = _topk_case(T, k, E, 64, 32, seed=61)
+    out = oracle.routed_fwd(x, ids, W, cap, topk=k)
+    dx = oracle.routed_dgrad(G, ids, W, cap, topk=k)
+    assert out.shape == (T * k, 32) and dx.shape == (T, 64)
+    for t in range(T):
+        qx, sx = oracle.quantize_rowwise(x[t:t + 1])
+        want_dx = np.zeros(64)
+        for j in range(k):
+            a = t * k + j
+            qw, sw = oracle.quantize_rowwise(W[ids[a]])
+            np.testing.assert_allclose(out[a], (oracle.dequant_rowwise(qx, sx) @ oracle.dequant_rowwise(qw, sw).T)[0],
+                                       rtol=1e-13, atol=1e-300)
+            qg, sg = oracle.quantize_rowwise(G[a:a + 1])
+            qwt, swt = oracle.quantize_colwise(W[ids[a]])
+            want_dx += (oracle.dequant_rowwise(qg, sg) @ oracle.dequant_rowwise(qwt, swt).T)[0]
+        np.testing.assert_allclose(dx[t], want_dx, rtol=1e-12, atol=1e-300)
+
+
+def test_topk_routed_wgrad_lossless_equals_exact_item_sum():
+    T, k, E, K, N = 30, 2, 3, 8, 4
+    rng = np.random.default_rng(62)
+    ids = rng.integers(0, E, size=T * k)
+    x, G = _pow2((T, K), 63), _pow2((T * k, N), 64)
+    got = oracle.routed_wgrad(G, x, ids, E, T * k + 31 * E, topk=k)
+    fx, fg = oracle.bf16_to_f64(x), oracle.bf16_to_f64(G)
+    for e in range(E):
+        items = [a for a in range(T * k) if ids[a] == e]
+        for n in range(N):
+            for kk in range(K):
+                exact = sum((Fraction(float(fg[a, n])) * Fraction(float(fx[a // k, kk])) for a in items), Fraction(0))
+                assert Fraction(float(got[e, n, kk])) == exact, (e, n, kk)
