@@ -552,12 +552,13 @@ def main():
         r_rows = torch.empty(cap, dtype=torch.int32, device=dev)
         r_pos = torch.empty(T, dtype=torch.int32, device=dev)
         r_status = torch.empty(1, dtype=torch.int32, device=dev)
+        r_ws = torch.empty(max(mx.mx_route_workspace_bytes(T, E), 4), dtype=torch.uint8, device=dev)
         ra, rg = dual_bufs(cap, K, cap), dual_bufs(cap, N, cap)
         out_t = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
         dx_t = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
 
         def routed():
-            mx.mx_route(ids_d, E, cap, r_offs, r_rows, r_pos, r_status)
+            mx.mx_route(ids_d, E, cap, r_offs, r_rows, r_pos, r_status, r_ws)
             qW, sW, qWt, sWt = mx.mx_quantize_weights(W, *wq)
             qA, sA, qAt, sAt = mx.mx_quantize_dual_gather(x_tok, r_rows, 1, cap, *ra)
             mx.mx_grouped_gemm_mx_rows(qA, sA, qW, sW, r_offs, r_rows, out=out_t)

@@ -253,9 +253,14 @@ mx_status mx_quantize_rowwise_gather(const uint16_t* x, int64_t src_rows, const 
  *              (such items join no group).
  * Requires 1 <= E <= 1024, 0 <= n < 2^30 and cap >= n + 31*E (the most rows
  * the padded groups can take; round it up to a multiple of 128 to use the
- * rows as the wgrad contraction).  Deterministic: one workgroup. */
+ * rows as the wgrad contraction).  ws: device scratch of at least
+ * mx_route_workspace_bytes(n, E) bytes, 4-byte aligned, the caller's; its
+ * contents need no initialisation and are not meaningful afterwards.  Three
+ * kernels (per-chunk histograms, one scan, per-chunk scatter); every grouped
+ * row follows from counts and ranks, so the result is deterministic. */
+size_t mx_route_workspace_bytes(int64_t n, int64_t E);
 mx_status mx_route(const int32_t* expert_idx, int64_t n, int64_t E, int64_t cap, int32_t* offs, int32_t* rows,
-                   int32_t* pos, int32_t* status, void* stream);
+                   int32_t* pos, int32_t* status, void* ws, size_t ws_bytes, void* stream);
 
 /* mx_quantize_dual on gathered rows: row r of the quantized operand is
  * x[rows[r] / topk, :], or a zero row where rows[r] is negative or

@@ -24,7 +24,7 @@ __all__ = [
     "OP_FWD", "OP_DGRAD", "OP_WGRAD", "OP_FWD_Q", "OP_DGRAD_Q", "SCALES_ROWMAJOR", "SCALES_GEMM",
     "mx_check_offsets", "check_offsets", "mx_grouped_mm_fwd_q_noalloc", "NOALLOC_SCRATCH_BYTES",
     "mx_route", "route_capacity", "mx_quantize_dual_gather", "mx_grouped_gemm_mx_rows", "mx_routed_experts",
-    "mx_topk_sum_rows",
+    "mx_topk_sum_rows", "mx_route_workspace_bytes",
 ]
 
 OP_FWD, OP_DGRAD, OP_WGRAD, OP_FWD_Q, OP_DGRAD_Q = 0, 1, 2, 3, 4
@@ -78,7 +78,9 @@ def load_library():
     lib.mx_topk_sum_rows.restype = c_int
     lib.mx_topk_sum_rows.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]
     lib.mx_route.restype = c_int
-    lib.mx_route.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]
+    lib.mx_route.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
+    lib.mx_route_workspace_bytes.restype = c_sz
+    lib.mx_route_workspace_bytes.argtypes = [c_i64, c_i64]
     lib.mx_quantize_dual_gather.restype = c_int
     lib.mx_quantize_dual_gather.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp,
                                             c_vp]
@@ -592,12 +594,13 @@ def route_capacity(n: int, E: int) -> int:
     return (int(n) + 31 * int(E) + 127) // 128 * 128
 
 
-def mx_route(expert_idx, E: int, cap: Optional[int] = None, offs=None, rows=None, pos=None, status=None):
+def mx_route(expert_idx, E: int, cap: Optional[int] = None, offs=None, rows=None, pos=None, status=None, ws=None):
     """Group routed items by expert on the device.  expert_idx int32 [n] (a
     top-k router's [T, k] ids flattened token-major).  Returns (offs int32 [E]
     padded END offsets, rows int32 [cap] grouped row -> item or -1, pos int32
     [n] item -> grouped row, status int32 [1]: 1 if an id lies outside
-    [0, E)).  Nothing is synchronized."""
+    [0, E)).  `ws`: uint8 scratch of mx_route_workspace_bytes(n, E) bytes
+    (allocated when None).  Nothing is synchronized."""
     import torch
     lib = load_library()
     _require(expert_idx, torch.int32, "expert_idx")
@@ -611,9 +614,17 @@ def mx_route(expert_idx, E: int, cap: Optional[int] = None, offs=None, rows=None
     rows = _out(rows, (cap,), torch.int32, dev, "rows")
     pos = _out(pos, (n,), torch.int32, dev, "pos")
     status = _out(status, (1,), torch.int32, dev, "status")
+    need = mx_route_workspace_bytes(n, E)
+    if ws is None:
+        ws = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    _require(ws, torch.uint8, "ws")
     _check("mx_route", lib.mx_route(_ptr(expert_idx), n, int(E), int(cap), _ptr(offs), _ptr(rows), _ptr(pos),
-                                    _ptr(status), _stream(dev)))
+                                    _ptr(status), _ptr(ws), ws.numel(), _stream(dev)))
     return offs, rows, pos, status
+
+
+def mx_route_workspace_bytes(n: int, E: int) -> int:
+    return int(load_library().mx_route_workspace_bytes(int(n), int(E)))
 
 
 def mx_quantize_dual_gather(x, rows, topk: int = 1, ldq: Optional[int] = None, q=None, s=None, q_t=None, s_t=None):

@@ -275,8 +275,13 @@ mx_status mx_topk_sum_rows(const float* x, int64_t T, int64_t k, int64_t cols, u
   return hip_status(mxk::launch_topk_sum(x, T, (int)k, cols, out, (hipStream_t)stream), fn);
 }
 
+size_t mx_route_workspace_bytes(int64_t n, int64_t E) {
+  if (n < 0 || E < 1 || E > mxk::kMaxExperts) return 0;
+  return mxk::route_ws_bytes(n, E);
+}
+
 mx_status mx_route(const int32_t* expert_idx, int64_t n, int64_t E, int64_t cap, int32_t* offs, int32_t* rows,
-                   int32_t* pos, int32_t* status, void* stream) {
+                   int32_t* pos, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "mx_route";
   if (E < 1 || E > mxk::kMaxExperts)
     return fail(MX_ERR_SHAPE, "%s: number of experts E=%lld outside [1, %d]", fn, (long long)E, mxk::kMaxExperts);
@@ -289,7 +294,13 @@ mx_status mx_route(const int32_t* expert_idx, int64_t n, int64_t E, int64_t cap,
     return fail(MX_ERR_NULL, "%s: null pointer", fn);
   if (!aligned(expert_idx, 4) || !aligned(offs, 4) || !aligned(rows, 4) || !aligned(pos, 4) || !aligned(status, 4))
     return fail(MX_ERR_ALIGN, "%s: int32 arrays must be 4-byte aligned", fn);
-  return hip_status(mxk::launch_route(expert_idx, n, E, cap, offs, rows, pos, status, (hipStream_t)stream), fn);
+  const size_t need = mxk::route_ws_bytes(n, E);
+  if (!ws || ws_bytes < need)
+    return fail(MX_ERR_WORKSPACE, "%s: workspace of %zu bytes at %p, need %zu (mx_route_workspace_bytes)", fn, ws_bytes,
+                ws, need);
+  if (!aligned(ws, 4)) return fail(MX_ERR_ALIGN, "%s: workspace must be 4-byte aligned", fn);
+  return hip_status(mxk::launch_route(expert_idx, n, E, cap, offs, rows, pos, status, (int32_t*)ws, (hipStream_t)stream),
+                    fn);
 }
 
 mx_status mx_check_offsets(const int32_t* offs, int64_t E, int64_t M, int32_t align, int32_t* status, void* stream) {

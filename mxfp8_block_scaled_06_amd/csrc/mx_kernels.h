@@ -57,9 +57,10 @@ hipError_t launch_quant_32x32(const uint16_t* x, int64_t rows_total, int64_t col
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t st);
 // out[t] = bf16(sum of the k fp32 rows x[t*k .. t*k+k-1]) (see mx_topk_sum_rows).
 hipError_t launch_topk_sum(const float* x, int64_t T, int k, int64_t cols, uint16_t* out, hipStream_t st);
-// Routing metadata (see mx_route).
-hipError_t launch_route(const int32_t* expert_idx, int64_t T, int64_t E, int64_t cap, int32_t* offs,
-                             int32_t* rows, int32_t* pos, int32_t* status, hipStream_t st);
+// Routing metadata (see mx_route); ws holds route_ws_bytes(n, E) bytes.
+size_t route_ws_bytes(int64_t n, int64_t E);
+hipError_t launch_route(const int32_t* expert_idx, int64_t n, int64_t E, int64_t cap, int32_t* offs, int32_t* rows,
+                        int32_t* pos, int32_t* status, int32_t* ws, hipStream_t st);
 // status[0] = validity bitmask of the group offsets (see mx_check_offsets).
 hipError_t launch_check_offsets(const int32_t* offs, int64_t E, int64_t M, int align, int32_t* status,
                                 hipStream_t st);

@@ -56,105 +56,170 @@ namespace mxk {
 //   rows [cap] grouped row -> item, -1 for padding and rows past the last group
 //   pos  [n]   item -> grouped row
 // status[0] gets 1 if some expert id lies outside [0, E) (those items are not
-// routed: pos = -1).  One workgroup of 1024 threads: a histogram, a scan of
-// the padded counts, then the items in chunks of 1024 in order, each item's
-// rank among the earlier items of its expert from wave ballots and a scan of
-// per-wave counts, so the result does not depend on thread timing.  The host
-// guarantees cap >= n + 31 * E, the most rows the padded groups can take.
+// routed: pos = -1).  Three passes over chunks of 1024 items, one workgroup
+// per chunk in the first and last:
+//   count   per-chunk histogram of expert ids (LDS atomics) -> cnt[chunk][E];
+//   scan    one workgroup: each expert's counts become exclusive prefixes over
+//           the chunks, the padded group sizes are scanned into the offsets,
+//           the padding rows get -1;
+//   scatter each item's rank among the earlier items of its expert in its
+//           chunk (wave ballots, then a scan of per-wave counts) plus the
+//           chunk's prefix and the group start is its grouped row.
+// Every position follows from counts and ranks, so the result does not depend
+// on thread timing.  The host guarantees cap >= n + 31 * E, the most rows the
+// padded groups can take.
 // ---------------------------------------------------------------------------
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ expert_idx, int T, int E,
-                                                                   int cap, int32_t* __restrict__ offs,
-                                                                   int32_t* __restrict__ rows,
-                                                                   int32_t* __restrict__ pos,
-                                                                   int32_t* __restrict__ status) {
+// Workspace: cnt [nchunks][E] | bad [nchunks] | start [E] (int32).
+struct RouteWs {
+  int32_t* cnt;
+  int32_t* bad;
+  int32_t* start;
+};
+
+__device__ __forceinline__ RouteWs route_ws(int32_t* ws, int nchunks, int E) {
+  RouteWs w;
+  w.cnt = ws;
+  w.bad = ws + (int64_t)nchunks * E;
+  w.start = w.bad + nchunks;
+  return w;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_count_kernel(const int32_t* __restrict__ expert_idx, int n,
+                                                                    int E, int32_t* __restrict__ ws) {
   __shared__ int cnt[kMaxExperts];
-  __shared__ int start[kMaxExperts];
-  __shared__ int run[kMaxExperts];
-  __shared__ int wc[kRouteWaves][kMaxExperts];
-  __shared__ int bad, total;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  for (int e = tid; e < E; e += kRouteThreads) {
-    cnt[e] = 0;
-    run[e] = 0;
-  }
+  __shared__ int bad;
+  const int tid = threadIdx.x, c = blockIdx.x;
+  const RouteWs w = route_ws(ws, gridDim.x, E);
+  for (int e = tid; e < E; e += kRouteThreads) cnt[e] = 0;
   if (tid == 0) bad = 0;
   __syncthreads();
-  for (int t = tid; t < T; t += kRouteThreads) {
-    const int e = expert_idx[t];
+  const int a = c * kRouteThreads + tid;
+  if (a < n) {
+    const int e = expert_idx[a];
     if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
     else bad = 1;
   }
   __syncthreads();
+  for (int e = tid; e < E; e += kRouteThreads) w.cnt[(int64_t)c * E + e] = cnt[e];
+  if (tid == 0) w.bad[c] = bad;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(int nchunks, int E, int cap,
+                                                                   int32_t* __restrict__ ws,
+                                                                   int32_t* __restrict__ offs,
+                                                                   int32_t* __restrict__ rows,
+                                                                   int32_t* __restrict__ status) {
+  __shared__ int wsum[kRouteWaves];
+  __shared__ int bad, total;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const RouteWs w = route_ws(ws, nchunks, E);
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  // expert e = tid: its counts become exclusive prefixes over the chunks
+  int cnt = 0;
+  if (tid < E) {
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = w.cnt[(int64_t)c * E + tid];
+      w.cnt[(int64_t)c * E + tid] = cnt;
+      cnt += v;
+    }
+  }
+  for (int c = tid; c < nchunks; c += kRouteThreads)
+    if (w.bad[c]) bad = 1;
   // exclusive scan of the padded counts (E <= 1024: one expert per thread)
-  {
-    const int e = tid;
-    const int pc = e < E ? (cnt[e] + 31) & ~31 : 0;
-    int incl = pc;
+  const int pc = tid < E ? (cnt + 31) & ~31 : 0;
+  int incl = pc;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(incl, d);
-      if (lane >= d) incl += v;
-    }
-    if (lane == 63) wc[0][wv] = incl;   // wave totals (wc reused as scratch)
-    __syncthreads();
-    int before = 0;
-    for (int w = 0; w < wv; ++w) before += wc[0][w];
-    if (e < E) {
-      start[e] = before + incl - pc;
-      offs[e] = before + incl;
-      // padding rows of this group
-      for (int r = start[e] + cnt[e]; r < before + incl; ++r) rows[r] = -1;
-    }
-    if (e == E - 1) total = before + incl;
-    __syncthreads();
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
   }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int x = 0; x < wv; ++x) before += wsum[x];
+  if (tid < E) {
+    const int st = before + incl - pc;
+    w.start[tid] = st;
+    offs[tid] = before + incl;
+    for (int r = st + cnt; r < before + incl; ++r) rows[r] = -1;   // this group's padding rows
+  }
+  if (tid == E - 1) total = before + incl;
+  __syncthreads();
   for (int r = total + tid; r < cap; r += kRouteThreads) rows[r] = -1;
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = 0; base < T; base += kRouteThreads) {
-    for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) wc[i / E][i % E] = 0;
-    __syncthreads();
-    const int t = base + tid;
-    const int e = t < T ? expert_idx[t] : -1;
-    const bool valid = e >= 0 && e < E;
-    int rank = 0;
-    uint64_t remaining = __ballot(valid);
-    while (remaining) {
-      const int leader = __builtin_ctzll(remaining);
-      const int le = __shfl(e, leader);
-      const uint64_t m = __ballot(valid && e == le);
-      if (valid && e == le) {
-        rank = __builtin_popcountll(m & lt);
-        if (lane == leader) wc[wv][le] = __builtin_popcountll(m);
-      }
-      remaining &= ~m;
-    }
-    __syncthreads();
-    // per expert: earlier waves of this chunk, plus earlier chunks
-    for (int x = tid; x < E; x += kRouteThreads) {
-      int acc = run[x];
-      for (int w = 0; w < kRouteWaves; ++w) {
-        const int c = wc[w][x];
-        wc[w][x] = acc;
-        acc += c;
-      }
-      run[x] = acc;
-    }
-    __syncthreads();
-    if (t < T) {
-      if (valid) {
-        const int p = start[e] + wc[wv][e] + rank;
-        pos[t] = p;
-        rows[p] = t;
-      } else {
-        pos[t] = -1;
-      }
-    }
-    __syncthreads();
-  }
   if (tid == 0) status[0] = bad;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(const int32_t* __restrict__ expert_idx, int n,
+                                                                      int E, const int32_t* __restrict__ ws,
+                                                                      int32_t* __restrict__ rows,
+                                                                      int32_t* __restrict__ pos) {
+  __shared__ int base[kMaxExperts];
+  __shared__ int wc[kRouteWaves][kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, c = blockIdx.x;
+  const RouteWs w = route_ws(const_cast<int32_t*>(ws), gridDim.x, E);
+  for (int e = tid; e < E; e += kRouteThreads) base[e] = w.start[e] + w.cnt[(int64_t)c * E + e];
+  for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) wc[i / E][i % E] = 0;
+  __syncthreads();
+  const int a = c * kRouteThreads + tid;
+  const int e = a < n ? expert_idx[a] : -1;
+  const bool valid = e >= 0 && e < E;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int rank = 0;
+  uint64_t remaining = __ballot(valid);
+  while (remaining) {
+    const int leader = __builtin_ctzll(remaining);
+    const int le = __shfl(e, leader);
+    const uint64_t m = __ballot(valid && e == le);
+    if (valid && e == le) {
+      rank = __builtin_popcountll(m & lt);
+      if (lane == leader) wc[wv][le] = __builtin_popcountll(m);
+    }
+    remaining &= ~m;
+  }
+  __syncthreads();
+  // per expert: exclusive prefix over the waves of this chunk
+  for (int x = tid; x < E; x += kRouteThreads) {
+    int acc = 0;
+    for (int v = 0; v < kRouteWaves; ++v) {
+      const int cv = wc[v][x];
+      wc[v][x] = acc;
+      acc += cv;
+    }
+  }
+  __syncthreads();
+  if (a < n) {
+    if (valid) {
+      const int p = base[e] + wc[wv][e] + rank;
+      pos[a] = p;
+      rows[p] = a;
+    } else {
+      pos[a] = -1;
+    }
+  }
+}
+
+size_t route_ws_bytes(int64_t n, int64_t E) {
+  const int64_t nchunks = (n + kRouteThreads - 1) / kRouteThreads;
+  return (size_t)(nchunks * E + nchunks + E) * sizeof(int32_t);
+}
+
+hipError_t launch_route(const int32_t* expert_idx, int64_t n, int64_t E, int64_t cap, int32_t* offs, int32_t* rows,
+                        int32_t* pos, int32_t* status, int32_t* ws, hipStream_t st) {
+  const int nchunks = (int)((n + kRouteThreads - 1) / kRouteThreads);
+  if (nchunks > 0) {
+    hipLaunchKernelGGL(route_count_kernel, dim3(nchunks), dim3(kRouteThreads), 0, st, expert_idx, (int)n, (int)E, ws);
+  }
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kRouteThreads), 0, st, nchunks, (int)E, (int)cap, ws, offs, rows,
+                     status);
+  if (nchunks > 0) {
+    hipLaunchKernelGGL(route_scatter_kernel, dim3(nchunks), dim3(kRouteThreads), 0, st, expert_idx, (int)n, (int)E,
+                       (const int32_t*)ws, rows, pos);
+  }
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -191,11 +256,5 @@ hipError_t launch_topk_sum(const float* x, int64_t T, int k, int64_t cols, uint1
   return hipGetLastError();
 }
 
-hipError_t launch_route(const int32_t* expert_idx, int64_t T, int64_t E, int64_t cap, int32_t* offs,
-                             int32_t* rows, int32_t* pos, int32_t* status, hipStream_t st) {
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, st, expert_idx, (int)T, (int)E, (int)cap,
-                     offs, rows, pos, status);
-  return hipGetLastError();
-}
 
 }  // namespace mxk

@@ -200,13 +200,18 @@ def test_offsets_check_validates_arguments():
 def test_routing_entry_points_validate():
     lib = _lib()
     r = lib.mx_route
-    assert r(FAKE, 100, 4, 100 + 31 * 4 - 1, FAKE, FAKE, FAKE, FAKE, None) == 2     # cap below n + 31 E
+    need = lib.mx_route_workspace_bytes(100, 4)
+    assert need >= 4 * (4 + 1 + 4) and lib.mx_route_workspace_bytes(-1, 4) == 0
+    ws = (FAKE, need)
+    assert r(FAKE, 100, 4, 100 + 31 * 4 - 1, FAKE, FAKE, FAKE, FAKE, *ws, None) == 2     # cap below n + 31 E
     assert "cap" in _err(lib)
-    assert r(FAKE, 100, 0, 1024, FAKE, FAKE, FAKE, FAKE, None) == 2                # E < 1
-    assert r(FAKE, 100, 1025, 1 << 16, FAKE, FAKE, FAKE, FAKE, None) == 2          # E > 1024
-    assert r(FAKE, -1, 4, 1024, FAKE, FAKE, FAKE, FAKE, None) == 2                 # n < 0
-    assert r(None, 100, 4, 1024, FAKE, FAKE, FAKE, FAKE, None) == 1                # null ids
-    assert r(FAKE, 100, 4, 1024, FAKE, FAKE + 2, FAKE, FAKE, None) == 3            # misaligned rows
+    assert r(FAKE, 100, 0, 1024, FAKE, FAKE, FAKE, FAKE, *ws, None) == 2                # E < 1
+    assert r(FAKE, 100, 1025, 1 << 16, FAKE, FAKE, FAKE, FAKE, *ws, None) == 2          # E > 1024
+    assert r(FAKE, -1, 4, 1024, FAKE, FAKE, FAKE, FAKE, *ws, None) == 2                 # n < 0
+    assert r(None, 100, 4, 1024, FAKE, FAKE, FAKE, FAKE, *ws, None) == 1                # null ids
+    assert r(FAKE, 100, 4, 1024, FAKE, FAKE + 2, FAKE, FAKE, *ws, None) == 3            # misaligned rows
+    assert r(FAKE, 100, 4, 1024, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == 4     # workspace too small
+    assert r(FAKE, 100, 4, 1024, FAKE, FAKE, FAKE, FAKE, None, need, None) == 4         # no workspace
     g = lib.mx_quantize_dual_gather
     assert g(FAKE, 10, FAKE, 0, 64, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == 2   # topk < 1
     assert g(FAKE, 10, FAKE, 1, 48, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == 2   # M % 32
