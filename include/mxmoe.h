@@ -164,6 +164,16 @@ mx_status mx_grouped_gemm_mx_f32(const uint8_t* X, const uint8_t* sX, const uint
                                  int scale_layout, const int32_t* offs, int mode, int64_t I, int64_t J, int64_t Kc,
                                  int64_t E, float* C, void* stream);
 
+/* mx_grouped_gemm_mx (bf16 output) with its workgroups dealt to output tiles
+ * in a seeded pseudo-random order instead of the library's (XCD-aware)
+ * order; order_seed = 0 is the library's order.  Every tile computes its
+ * outputs alone, so the result is bit-identical for every seed: the race
+ * check of the test suite compares seeds, which changes which tiles run side
+ * by side and in what sequence. */
+mx_status mx_grouped_gemm_mx_ordered(const uint8_t* X, const uint8_t* sX, const uint8_t* Y, const uint8_t* sY,
+                                     int scale_layout, const int32_t* offs, int mode, int64_t I, int64_t J, int64_t Kc,
+                                     int64_t E, uint16_t* C, uint64_t order_seed, void* stream);
+
 /* ------------------------------------------------------------------------
  * Validity of group offsets, tested on the device (no host round trip; the
  * caller reads *status when it chooses to).  offs: int32 [E] cumulative END

@@ -70,6 +70,9 @@ def load_library():
         f = getattr(lib, name)
         f.restype = c_int
         f.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, c_vp, c_int, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp]
+    lib.mx_grouped_gemm_mx_ordered.restype = c_int
+    lib.mx_grouped_gemm_mx_ordered.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, c_vp, c_int, c_i64, c_i64, c_i64, c_i64,
+                                               c_vp, ctypes.c_uint64, c_vp]
     lib.mx_grouped_gemm_mx_rows.restype = c_int
     lib.mx_grouped_gemm_mx_rows.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp,
                                             c_vp, c_i64, c_vp]
@@ -315,6 +318,19 @@ def mx_topk_sum_rows(x, k: int, out=None):
     T, cols = x.shape[0] // k, x.shape[1]
     out = _out(out, (T, cols), torch.bfloat16, x.device, "out")
     _check("mx_topk_sum_rows", lib.mx_topk_sum_rows(_ptr(x), T, int(k), cols, _ptr(out), _stream(x.device)))
+    return out
+
+
+def mx_grouped_gemm_mx_ordered(X, sX, Y, sY, offs, mode: int, order_seed: int, out=None):
+    """mx_grouped_gemm_mx (bf16) with workgroups dealt to tiles in a seeded
+    pseudo-random order (race checks: the result must not depend on it)."""
+    import torch
+    lib = load_library()
+    I, J, Kc, E, layout = _gemm_operands(X, sX, Y, sY, offs, mode, "gemm")
+    out = _out(out, (I, J) if mode == 0 else (E, I, J), torch.bfloat16, X.device, "out")
+    _check("mx_grouped_gemm_mx_ordered",
+           lib.mx_grouped_gemm_mx_ordered(_ptr(X), _ptr(sX), _ptr(Y), _ptr(sY), layout, _ptr(offs), mode, I, J, Kc, E,
+                                          _ptr(out), int(order_seed), _stream(X.device)))
     return out
 
 

@@ -168,7 +168,7 @@ namespace {
 mx_status grouped_gemm_impl(const char* fn, const uint8_t* X, const uint8_t* sX, const uint8_t* Y,
                             const uint8_t* sY, int scale_layout, const int32_t* offs, int mode, int64_t I, int64_t J,
                             int64_t Kc, int64_t E, void* C, int out_f32, void* stream,
-                            const int32_t* row_map = nullptr, int64_t c_rows = -1) {
+                            const int32_t* row_map = nullptr, int64_t c_rows = -1, uint64_t order_seed = 0) {
   if (scale_layout == MX_SCALES_ROWMAJOR)
     return fail(MX_ERR_LAYOUT,
                 "%s: the GEMM reads scales in its blocked layout [K/128][rows][4]; row-major scales "
@@ -216,6 +216,12 @@ mx_status grouped_gemm_impl(const char* fn, const uint8_t* X, const uint8_t* sX,
   a.c_estride = I * J;
   a.row_map = row_map;
   a.c_rows = row_map ? c_rows : I;
+  if (order_seed) {
+    // large primes: coprime with every grid size the launch can have (< 2^31)
+    static const int64_t kPrimes[4] = {2147483647LL, 1000000007LL, 998244353LL, 1000003LL};
+    a.order_mul = kPrimes[order_seed % 4];
+    a.order_add = (int64_t)((order_seed / 4) % 1000003ULL);
+  }
   return hip_status(mxk::launch_grouped_gemm(a, (hipStream_t)stream), fn);
 }
 
@@ -301,6 +307,13 @@ mx_status mx_route(const int32_t* expert_idx, int64_t n, int64_t E, int64_t cap,
   if (!aligned(ws, 4)) return fail(MX_ERR_ALIGN, "%s: workspace must be 4-byte aligned", fn);
   return hip_status(mxk::launch_route(expert_idx, n, E, cap, offs, rows, pos, status, (int32_t*)ws, (hipStream_t)stream),
                     fn);
+}
+
+mx_status mx_grouped_gemm_mx_ordered(const uint8_t* X, const uint8_t* sX, const uint8_t* Y, const uint8_t* sY,
+                                     int scale_layout, const int32_t* offs, int mode, int64_t I, int64_t J, int64_t Kc,
+                                     int64_t E, uint16_t* C, uint64_t order_seed, void* stream) {
+  return grouped_gemm_impl("mx_grouped_gemm_mx_ordered", X, sX, Y, sY, scale_layout, offs, mode, I, J, Kc, E, C, 0,
+                           stream, nullptr, -1, order_seed);
 }
 
 mx_status mx_check_offsets(const int32_t* offs, int64_t E, int64_t M, int32_t align, int32_t* status, void* stream) {

@@ -146,6 +146,13 @@ __device__ __forceinline__ int64_t tile_of_workgroup(int64_t b) {
   return ((i / kXcdChunk) * 8 + (b & 7)) * kXcdChunk + i % kXcdChunk;
 }
 
+// Tile of workgroup b: the XCD-aware order, or (race checks) a seeded
+// bijection of it over the grid (mul is coprime with the grid size).
+__device__ __forceinline__ int64_t ordered_tile(const GemmArgs& a, int64_t b) {
+  const int64_t t = tile_of_workgroup(b);
+  return a.order_mul ? (int64_t)(((uint64_t)t * (uint64_t)a.order_mul + (uint64_t)a.order_add) % gridDim.x) : t;
+}
+
 template <int MODE>
 __device__ __forceinline__ TileDesc decode_tile(const GemmArgs& a, int* s_offs, int* s_pref, int* s_misc) {
   TileDesc d;
@@ -162,7 +169,7 @@ __device__ __forceinline__ TileDesc decode_tile(const GemmArgs& a, int* s_offs, 
     __syncthreads();
     const int64_t total_m = s_misc[0];
     const int64_t total = total_m * ntj;
-    const int64_t t = tile_of_workgroup(blockIdx.x);
+    const int64_t t = ordered_tile(a, blockIdx.x);
     if (t >= total) return d;
     // Inside a band of `width` N-tiles, expert e owns positions
     // [pref[e] * width, pref[e+1] * width): its N-tiles in turn, and for each
@@ -200,7 +207,7 @@ __device__ __forceinline__ TileDesc decode_tile(const GemmArgs& a, int* s_offs, 
     const int64_t nti = (a.I + kBM - 1) / kBM;
     const int64_t per_e = nti * ntj;
     const int64_t total = per_e * a.E;
-    const int64_t t = tile_of_workgroup(blockIdx.x);
+    const int64_t t = ordered_tile(a, blockIdx.x);
     if (t >= total) return d;
     const int e = (int)(t / per_e);
     const int64_t r = t - e * per_e;

@@ -28,6 +28,8 @@ struct GemmArgs {
   int64_t c_estride;          // mode 1: elements between experts of C
   const int32_t* row_map;     // mode 0, optional: X row i is stored to C row row_map[i] (skipped if outside [0, c_rows))
   int64_t c_rows;
+  int64_t order_mul;          // 0: the library's tile order; else workgroup slot t runs tile (t * mul + add) % grid
+  int64_t order_add;
 };
 
 // gemm_rows_per_batch == 0: row-major scales [rows_total][cols/32]; > 0:

@@ -226,6 +226,14 @@ def test_routing_entry_points_validate():
     assert m(FAKE, FAKE, FAKE, FAKE, mx.SCALES_ROWMAJOR, FAKE, 256, 128, 128, 2, FAKE, FAKE, 10, None) == 6
 
 
+def test_ordered_gemm_validates_like_the_gemm():
+    lib = _lib()
+    o = lib.mx_grouped_gemm_mx_ordered
+    assert o(FAKE, FAKE, FAKE, FAKE, mx.SCALES_GEMM, FAKE, 0, 256, 128, 100, 2, FAKE, 7, None) == 2   # Kc % 128
+    assert o(FAKE, FAKE, FAKE, FAKE, mx.SCALES_ROWMAJOR, FAKE, 0, 256, 128, 128, 2, FAKE, 7, None) == 6
+    assert o(None, FAKE, FAKE, FAKE, mx.SCALES_GEMM, FAKE, 0, 256, 128, 128, 2, FAKE, 7, None) == 1
+
+
 def test_topk_entry_points_validate():
     lib = _lib()
     t = lib.mx_topk_sum_rows

@@ -185,6 +185,42 @@ def test_gemm_deterministic_and_errors():
         mx.mx_grouped_mm_wgrad(to_dev_bf16(x.A[:250]), to_dev_bf16(x.A[:250]), offs)
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+def test_tile_order_does_not_change_results(mode):
+    """Race check: workgroups dealt to tiles in seeded pseudo-random orders
+    (so different tiles share the chip, in a different sequence) give
+    bit-identical outputs, ragged and empty groups included, and the same as
+    the repeated default order."""
+    torch = require_gpu()
+    import mxfp8_block_scaled_06_amd as mx
+    rng = np.random.default_rng(720 + mode)
+    if mode == 0:
+        counts = [300, 0, 1, 511, 45, 0, 900, 32]
+        I, J, Kc, E = sum(counts), 520, 640, len(counts)
+        X, Y = _random_codes(rng, (I, Kc)), _random_codes(rng, (E, J, Kc))
+        sX = rng.integers(112, 142, size=(I, Kc // 32)).astype(np.uint8)
+        sY = rng.integers(112, 142, size=(E, J, Kc // 32)).astype(np.uint8)
+    else:
+        counts = [96, 32, 0, 480, 64, 0, 320]
+        I, J, E = 520, 392, len(counts)
+        Kc = 1024
+        X, Y = _random_codes(rng, (I, Kc)), _random_codes(rng, (J, Kc))
+        sX = rng.integers(112, 142, size=(I, Kc // 32)).astype(np.uint8)
+        sY = rng.integers(112, 142, size=(J, Kc // 32)).astype(np.uint8)
+    offs = inp.offsets_from_counts(counts)
+    log(f"tile order mode={mode} counts={counts}")
+    args = (to_dev_u8(X), mx.mx_scales_to_gemm_layout(to_dev_u8(sX)), to_dev_u8(Y),
+            mx.mx_scales_to_gemm_layout(to_dev_u8(sY)), to_dev_i32(offs), mode)
+    ref = mx.mx_grouped_gemm_mx(*args)
+    for seed in [0, 1, 2, 3, 4, 5, 6, 7, 12345, 2 ** 40 + 3]:
+        got = mx.mx_grouped_gemm_mx_ordered(*args, seed)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), seed
+    # and the default order is reproducible launch after launch
+    for _ in range(3):
+        assert torch.equal(mx.mx_grouped_gemm_mx(*args).view(torch.int16), ref.view(torch.int16))
+
+
 def test_gemm_refuses_row_major_scales():
     """The scale layout travels with the data (its shape) and through the C
     ABI (the layout argument): row-major scales raise a clear error."""
