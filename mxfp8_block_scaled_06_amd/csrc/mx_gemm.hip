@@ -39,7 +39,10 @@
 //    next window.  One barrier per stage, at the start of its second window:
 //    every wave has then finished reading the stage's buffer, which receives
 //    the DMA of the stage after next (issued one load per MFMA across the
-//    window), and the next stage has landed.
+//    window), and the next stage has landed.  Fragment addresses are a
+//    per-lane base (row and swizzled piece) per window and operand plus a
+//    constant: the 32-row sub-tile rides in the LDS immediate offset, so the
+//    loop spends about a dozen vector adds per stage on addressing.
 //  * Tile scheduler on the device: the group offsets never cross to the host.
 //    Mode 0 enumerates (expert, M-tile) pairs from the offsets; tiles are
 //    ordered in bands of 8 N-tiles, expert by expert inside a band with all
@@ -310,17 +313,6 @@ struct Frag {
   int s;
 };
 
-// Read the operand of one 32-row sub-tile (this lane's `row`) for MFMA window
-// `w` (0/1) of a stage: pieces 4w + half and 4w + half + 2 of the row, and
-// the scale byte of block 2w + half from the stage's [rows][4] scale chunk.
-__device__ __forceinline__ void read_frag(const uint8_t* tile, const uint8_t* sc, int row, int pa, int pb, int w,
-                                          int half, Frag& f) {
-  const v4i a0 = *(const v4i*)(tile + row * kBK + pa);
-  const v4i a1 = *(const v4i*)(tile + row * kBK + pb);
-  f.s = sc[row * 4 + 2 * w + half];
-  f.v = (v8i){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-}
-
 // Contraction-block mask of one MFMA window (wgrad: blocks of a stage that
 // lie outside the expert's group).  keep0/keep1 cover the window's two
 // blocks (the fragment's first and second 16-byte piece); `sel` is the byte
@@ -443,13 +435,27 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
     // read has a whole window of MFMAs to land.
     Frag F0[8], F1[8];
     // fragment `f` of window `w` of the stage in LDS buffer `st`
-    auto read = [&](const uint8_t* st, int w, int f, Frag& dst) {
-      if (f < 4) {
-        read_frag(st, st + 2 * kTileBytes, xrow0 + 32 * f, pc[w][0], pc[w][1], w, half, dst);
-      } else {
-        read_frag(st + kTileBytes, st + 2 * kTileBytes + 2 * kScaleChunk, yrow0 + 32 * (f - 4), pc[w][0], pc[w][1], w,
-                  half, dst);
+    // this lane's byte offsets inside a stage buffer: the fragment's 32-row
+    // sub-tile then only adds a constant (an LDS immediate offset)
+    int xo[2][2], yo[2][2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        xo[w][c] = xrow0 * kBK + pc[w][c];
+        yo[w][c] = kTileBytes + yrow0 * kBK + pc[w][c];
       }
+    const int sxo = 2 * kTileBytes + xrow0 * 4 + half, syo = 2 * kTileBytes + 2 * kScaleChunk + yrow0 * 4 + half;
+    auto read = [&](const uint8_t* st, int w, int f, Frag& dst) {
+      const bool isx = f < 4;
+      const int sub = isx ? f : f - 4;
+      const uint8_t* p0 = st + (isx ? xo[w][0] : yo[w][0]) + sub * 32 * kBK;
+      const uint8_t* p1 = st + (isx ? xo[w][1] : yo[w][1]) + sub * 32 * kBK;
+      const uint8_t* ps = st + (isx ? sxo : syo) + sub * 32 * 4 + 2 * w;
+      const v4i a0 = *(const v4i*)p0;
+      const v4i a1 = *(const v4i*)p1;
+      dst.s = *ps;
+      dst.v = (v8i){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     };
     // wgrad masking is applied where a fragment is first used, not where it
     // is read: an LDS wait right after each read would stall the MFMAs the
