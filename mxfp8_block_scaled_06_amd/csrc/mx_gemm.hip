@@ -30,16 +30,20 @@
 //    read as zeros without clamping code.  Scales use the GEMM layout
 //    [K/128][rows][4] so one stage's scales for 256 rows are one 1 KiB line
 //    run per operand.
-//  * LDS bandwidth bounds this loop: a stage moves 64 KiB of DMA writes and
-//    128 KiB of fragment reads through the LDS, and measured on gfx950 the
-//    two serialize to about as long as the stage's 32 MFMAs per wave.  So
-//    MFMAs must never wait on a fragment read queued behind DMA writes: the
-//    fragments of the two MFMA windows of a stage live in two register sets,
-//    and while one window's 16 MFMAs run the other set is refilled for the
-//    next window.  One barrier per stage, at the start of its second window:
-//    every wave has then finished reading the stage's buffer, which receives
-//    the DMA of the stage after next (issued one load per MFMA across the
-//    window), and the next stage has landed.  Fragment addresses are a
+//  * The operand stream bounds this loop: a stage moves 66 KiB per CU from
+//    L2 into LDS through the CU's texture data path, which on gfx950 takes
+//    about three quarters as long as the stage's 32 MFMAs per wave and
+//    overlaps with them only in part (counters show that path busy ~80% of
+//    the kernel's cycles, the LDS ~15%).  A 256 x 256 tile is the largest
+//    whose fp32 accumulators fit a CU's registers, so the bytes per flop
+//    cannot drop; what the loop can do is keep the MFMAs fed while the
+//    stream runs.  MFMAs must never wait on a fragment read queued behind
+//    DMA writes: the fragments of the two MFMA windows of a stage live in
+//    two register sets, and while one window's 16 MFMAs run the other set is
+//    refilled for the next window.  One barrier per stage, at the start of
+//    its second window: every wave has then finished reading the stage's
+//    buffer, which receives the DMA of the stage after next (issued one load
+//    per MFMA across the window), and the next stage has landed.  Fragment addresses are a
 //    per-lane base (row and swizzled piece) per window and operand plus a
 //    constant: the 32-row sub-tile rides in the LDS immediate offset, so the
 //    loop spends about a dozen vector adds per stage on addressing.
