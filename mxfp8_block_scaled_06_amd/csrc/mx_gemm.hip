@@ -22,8 +22,8 @@
 //    row; trading runs with lane l ^ 32 gives 8-column (16-byte) pieces,
 //    which the bf16 epilogue stages through the idle LDS so the global
 //    stores write whole 512-byte row segments.
-//  * Workgroup tile 256 x 256, 4 waves of 128 x 128 (4x4 MFMA tiles each,
-//    256 fp32 accumulators per lane in AGPRs).  Stages of 128 contraction
+//  * Workgroup tile 256 x 256, 8 waves (two per SIMD) of 128 x 64 (4 x 2
+//    MFMA tiles each, 128 fp32 accumulators per lane).  Stages of 128 contraction
 //    bytes: every row moves as one full 128-byte line, HBM/L2 -> LDS by
 //    buffer_load ... lds (no VGPR staging), two stages of 68 KiB in LDS.
 //    Buffer descriptors end at the last valid row, so rows past a group end
@@ -32,18 +32,22 @@
 //    run per operand.
 //  * The operand stream bounds this loop: a stage moves 66 KiB per CU from
 //    L2 into LDS through the CU's texture data path, which on gfx950 takes
-//    about three quarters as long as the stage's 32 MFMAs per wave and
-//    overlaps with them only in part (counters show that path busy ~80% of
-//    the kernel's cycles, the LDS ~15%).  A 256 x 256 tile is the largest
-//    whose fp32 accumulators fit a CU's registers, so the bytes per flop
-//    cannot drop; what the loop can do is keep the MFMAs fed while the
-//    stream runs.  MFMAs must never wait on a fragment read queued behind
-//    DMA writes: the fragments of the two MFMA windows of a stage live in
-//    two register sets, and while one window's 16 MFMAs run the other set is
-//    refilled for the next window.  One barrier per stage, at the start of
-//    its second window: every wave has then finished reading the stage's
-//    buffer, which receives the DMA of the stage after next (issued one load
-//    per MFMA across the window), and the next stage has landed.  Fragment addresses are a
+//    about three quarters as long as the stage's MFMAs and overlaps with
+//    them only in part (counters show that path busy ~80% of the kernel's
+//    cycles, the LDS ~15%).  A 256 x 256 tile is the largest whose fp32
+//    accumulators fit a CU's registers, so the bytes per flop cannot drop;
+//    the loop is built to keep the matrix cores fed while the stream runs.
+//    Waves 0..3 (one per SIMD: the hardware deals a workgroup's waves
+//    round-robin over the SIMDs) issue all of the DMA; waves 4..7 only read
+//    LDS and run MFMAs, so while a loading wave waits on a full address
+//    queue the other wave of its SIMD keeps the matrix core busy.  Each
+//    wave reads the next window's fragments while the current window's
+//    MFMAs run: its X sub-tile registers are refilled right after their last
+//    MFMA of the window, its Y sub-tiles alternate between two register
+//    sets.  One barrier per stage, at the start of its second window: every
+//    wave has then finished reading the stage's buffer, which receives the
+//    DMA of the stage after next (two loads per MFMA of the loading waves
+//    across the window), and the next stage has landed.  Fragment addresses are a
 //    per-lane base (row and swizzled piece) per window and operand plus a
 //    constant: the 32-row sub-tile rides in the LDS immediate offset, so the
 //    loop spends about a dozen vector adds per stage on addressing.
@@ -72,13 +76,13 @@ namespace mxk {
 constexpr int kBM = 256;        // output rows per tile (rows of X)
 constexpr int kBN = 256;        // output cols per tile (rows of Y)
 constexpr int kBK = 128;        // contraction bytes per stage (4 scale blocks, 2 MFMA windows)
-constexpr int kThreads = 256;   // 4 waves, 2 x 2 arrangement of 128 x 128
+constexpr int kThreads = 512;   // 8 waves (two per SIMD), 2 x 4 arrangement of 128 x 64 blocks
 constexpr int kBand = 8;        // N-tiles per band in the tile order
 constexpr int kXcdChunk = 16;   // consecutive tiles of the order dealt to one XCD at a time
 constexpr int kTileBytes = kBM * kBK;             // 32 KiB per operand tile
 constexpr int kScaleChunk = kBM * 4;              // one [rows][4] scale chunk: 1 KiB
 constexpr int kStageBytes = 2 * kTileBytes + 4 * kScaleChunk;
-constexpr int kDmaPerStage = 8 + 8 + 1;           // per wave: X data, Y data, one scale chunk
+constexpr int kDmaPerStage = 8 + 8 + 1;           // per loading wave (0..3): X data, Y data, one scale chunk
 constexpr int kMaxExpertsLds = 1024;
 constexpr int kOutPitch = kBN * 2 + 16;          // bytes per staged bf16 output row (+16: spreads banks)
 constexpr int kRsrcWord3 = 0x00020000;            // raw buffer, 32-bit elements (gfx9 family)
@@ -256,12 +260,13 @@ struct LoadState {
 };
 
 // DMA of one stage (contraction bytes [k0 + 128*stage_no, +128)) into LDS
-// buffer `buf`: per wave 8 + 8 one-KiB data loads (rows 64*wv .. +63 of X and
-// Y) and one scale load: stages start on a multiple of 128 bytes, so a
-// stage's scales are the single 1 KiB chunk q = kk / 128 per operand, loaded
-// by wave 0 (X) and wave 2 (Y); waves 1 and 3 issue an empty load.  Stages at
-// or past `ns` get empty ranges: no data moves, but every wave still issues
-// its 17 loads so the vmcnt bookkeeping is the same for every stage.
+// buffer `buf`, issued by the loading waves wv = 0..3: per wave 8 + 8 one-KiB
+// data loads (rows 64*wv .. +63 of X and Y) and one scale load: stages start
+// on a multiple of 128 bytes, so a stage's scales are the single 1 KiB chunk
+// q = kk / 128 per operand, loaded by wave 0 (X) and wave 2 (Y); waves 1 and
+// 3 issue an empty load into their own slot.  Stages at or past `ns` get
+// empty ranges: no data moves, but every loading wave still issues its 17
+// loads so the vmcnt bookkeeping is the same for every stage.
 struct StageDma {
   __amdgpu_buffer_rsrc_t rx, ry, rs;
   uint8_t* st;
@@ -388,7 +393,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = uni32(tid >> 6);
-  const int iw = wv >> 1, jw = wv & 1;   // wave's 128x128 quadrant: rows iw, cols jw
+  const int iw = wv >> 2, jw = wv & 3;   // wave's 128 x 64 block: X rows iw * 128, Y rows jw * 64
   const int half = lane >> 5, l32 = lane & 31;
 
   // tile description, made wave-uniform (it is identical for every thread)
@@ -413,15 +418,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
   L.nchunks = a.Kc / kBK;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const int row = (wv * 8 + u) * 8 + (lane >> 3);
+    const int row = ((wv & 3) * 8 + u) * 8 + (lane >> 3);
     L.voff[u] = row * (int)a.ldx + (((lane & 7) ^ piece_swz(row)) << 4);
   }
 
-  v16f acc[4][4];
+  v16f acc[2][4];
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int y = 0; y < 2; ++y)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = (v16f){};
+    for (int x = 0; x < 4; ++x) acc[y][x] = (v16f){};
 
   const int ns = (int)((k1 - k0 + kBK - 1) / kBK);
   if (ns > 0) {
@@ -432,15 +437,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
     for (int w = 0; w < 2; ++w)
 #pragma unroll
       for (int c = 0; c < 2; ++c) pc[w][c] = ((4 * w + half + 2 * c) ^ sw) << 4;
-    const int yrow0 = jw * 128 + l32, xrow0 = iw * 128 + l32;
-    // Operand sets of the two MFMA windows of a stage: [0..3] X sub-tiles,
-    // [4..7] Y sub-tiles.  While one window's 16 MFMAs run from one set, the
-    // other set is refilled from LDS for the next window, so every fragment
-    // read has a whole window of MFMAs to land.
-    Frag F0[8], F1[8];
-    // fragment `f` of window `w` of the stage in LDS buffer `st`
-    // this lane's byte offsets inside a stage buffer: the fragment's 32-row
-    // sub-tile then only adds a constant (an LDS immediate offset)
+    const int yrow0 = jw * 64 + l32, xrow0 = iw * 128 + l32;
+    // Operands: X sub-tiles qx = 0..3 in FX[0..2] and FX[3 + window] (the last
+    // X sub-tile alternates between two registers so its refill never waits
+    // for the window's last MFMA), Y sub-tiles qy = 0..1 in FY[window][qy].
+    // A window's MFMAs run X sub-tile by X sub-tile, so FX[qx] is refilled for
+    // the next window right after its second MFMA.
+    Frag FX[5], FY[2][2];
     int xo[2][2], yo[2][2];
 #pragma unroll
     for (int w = 0; w < 2; ++w)
@@ -450,9 +453,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
         yo[w][c] = kTileBytes + yrow0 * kBK + pc[w][c];
       }
     const int sxo = 2 * kTileBytes + xrow0 * 4 + half, syo = 2 * kTileBytes + 2 * kScaleChunk + yrow0 * 4 + half;
-    auto read = [&](const uint8_t* st, int w, int f, Frag& dst) {
-      const bool isx = f < 4;
-      const int sub = isx ? f : f - 4;
+    // sub-tile `sub` of operand X (isx) or Y, window `w`, stage buffer `st`
+    auto read = [&](const uint8_t* st, int w, bool isx, int sub, Frag& dst) {
       const uint8_t* p0 = st + (isx ? xo[w][0] : yo[w][0]) + sub * 32 * kBK;
       const uint8_t* p1 = st + (isx ? xo[w][1] : yo[w][1]) + sub * 32 * kBK;
       const uint8_t* ps = st + (isx ? sxo : syo) + sub * 32 * 4 + 2 * w;
@@ -461,28 +463,60 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
       dst.s = *ps;
       dst.v = (v8i){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     };
-    // wgrad masking is applied where a fragment is first used, not where it
-    // is read: an LDS wait right after each read would stall the MFMAs the
-    // read is meant to overlap
-    auto first_use = [&](Frag* F, int m, const WinMask& mk) {
-      const int qx = m >> 2, qy = m & 3;
-      if (qx == 0) mask_frag(F[4 + qy], mk);
-      if (qy == 0) mask_frag(F[qx], mk);
-    };
-    // refill order: what the next window's first MFMAs need comes first
-    constexpr int kOrder[8] = {0, 4, 5, 6, 7, 1, 2, 3};
 
-    // One stage.  NXS = X sub-tiles of this wave that hold rows of the tile
-    // (a group's last M-tile may be partial: MFMAs and fragment reads of
-    // sub-tiles past its end are not compiled in); MASK = the stage has
-    // contraction blocks outside the wgrad group.  Each variant is one
-    // straight-line block, so its schedule is the one written here.
-    auto stage = [&](auto nxs_c, auto mask_c, int kt) __attribute__((always_inline)) {
+    // One MFMA window: MFMA m = (qx = m / 2, qy = m % 2) from the current
+    // registers while the next window's operands are read from `src`
+    // (window NW of that stage buffer); with LOADS (a loading wave's second
+    // window), DMA loads 2m and 2m + 1 of the stage after next go out with
+    // MFMA m, the scale chunk with the first.  NXS = X sub-tiles of this wave
+    // that hold rows of the tile (a group's last M-tile may be partial: MFMAs
+    // and fragment reads of sub-tiles past its end are not compiled in);
+    // MASK = the stage has contraction blocks outside the wgrad group, zeroed
+    // where a fragment is first used rather than where it is read (an LDS
+    // wait right after each read would stall the MFMAs the read overlaps).
+    // Each variant is one straight-line block, so its schedule is the one
+    // written here.
+    auto window = [&](auto w_c, auto nxs_c, auto mask_c, auto loads_c, const uint8_t* src, const WinMask& mk,
+                      const StageDma& pend) __attribute__((always_inline)) {
+      constexpr int W = decltype(w_c)::value, NW = W ^ 1;
       constexpr int NXS = decltype(nxs_c)::value;
       constexpr bool MASK = decltype(mask_c)::value;
+      constexpr bool LOADS = decltype(loads_c)::value;
+      static_for<0, 8>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        constexpr int qx = m >> 1, qy = m & 1;
+        constexpr int xi = qx < 3 ? qx : 3 + W;
+        if constexpr (qx < NXS) {
+          if constexpr (MASK) {
+            if (qy == 0) mask_frag(FX[xi], mk);
+            if (qx == 0) mask_frag(FY[W][qy], mk);
+          }
+          acc[qy][qx] = mfma(FY[W][qy], FX[xi], acc[qy][qx]);
+        }
+        if constexpr (LOADS) {
+          issue_load<2 * m>(pend, L, wv, lane);
+          issue_load<2 * m + 1>(pend, L, wv, lane);
+          if constexpr (m == 0) issue_load<16>(pend, L, wv, lane);
+        }
+        if constexpr (NXS > 0) {
+          if constexpr (m < 2) read(src, NW, false, m, FY[NW][m]);
+          if constexpr (m == 0 && NXS > 3) read(src, NW, true, 3, FX[3 + NW]);
+          if constexpr (m == 1 || m == 3 || m == 5) {
+            if constexpr ((m >> 1) < NXS) read(src, NW, true, m >> 1, FX[m >> 1]);
+          }
+        }
+        MX_FENCE();
+      });
+    };
+
+    // One stage: window 0 from the registers (reading window 1 of this
+    // stage), barrier, window 1 (reading window 0 of the next stage; loading
+    // waves issue the DMA of the stage after next into this stage's buffer).
+    auto stage = [&](auto nxs_c, auto mask_c, auto dma_c, int kt) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_c)::value;
       const int buf = kt & 1;
-      const uint8_t* cs = smem + buf * kStageBytes;           // this stage
-      const uint8_t* nst = smem + (buf ^ 1) * kStageBytes;    // next stage
+      const uint8_t* cs = smem + buf * kStageBytes;
+      const uint8_t* nst = smem + (buf ^ 1) * kStageBytes;
       const int64_t kk = k0 + (int64_t)kt * kBK;
       WinMask mk0{}, mk1{};
       if (MASK) {
@@ -490,65 +524,40 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
         mk0 = make_mask(nvalid, 0, half);
         mk1 = make_mask(nvalid, 1, half);
       }
-      // ---- window 0 of stage kt from F0; F1 <- window 1 of stage kt ----
-      static_for<0, 16>([&](auto mc) {
-        constexpr int m = decltype(mc)::value;
-        constexpr int qx = m >> 2, qy = m & 3;
-        if constexpr (qx < NXS) {
-          if constexpr (MASK) first_use(F0, m, mk0);
-          acc[qy][qx] = mfma(F0[4 + qy], F0[qx], acc[qy][qx]);
-        }
-        if constexpr (m < 8) {
-          constexpr int f = kOrder[m];
-          if constexpr (f < 4 ? f < NXS : NXS > 0) read(cs, 1, f, F1[f]);
-        }
-        MX_FENCE();
-      });
-      // ---- window 1 of stage kt from F1; F0 <- window 0 of stage kt+1;
-      // ---- DMA of stage kt+2 into this stage's buffer ----
+      const StageDma none{};
+      window(std::integral_constant<int, 0>{}, nxs_c, mask_c, std::false_type{}, cs, mk0, none);
       stage_barrier();   // stage kt+1 landed; every wave is done reading buffer `buf`
       const StageDma pend = make_stage_dma(smem, buf, L, k0, kt + 2, ns, wv);
-      static_for<0, 16>([&](auto mc) {
-        constexpr int m = decltype(mc)::value;
-        constexpr int qx = m >> 2, qy = m & 3;
-        if constexpr (qx < NXS) {
-          if constexpr (MASK) first_use(F1, m, mk1);
-          acc[qy][qx] = mfma(F1[4 + qy], F1[qx], acc[qy][qx]);
-        }
-        // one load per MFMA (the scale chunk with the first): the four
-        // waves' loads then arrive at the address unit about as fast as it
-        // takes them, and no wave stalls on a full queue in front of an MFMA
-        issue_load<m>(pend, L, wv, lane);
-        if constexpr (m == 0) issue_load<16>(pend, L, wv, lane);
-        if constexpr (m < 8) {
-          constexpr int f = kOrder[m];
-          if constexpr (f < 4 ? f < NXS : NXS > 0) read(nst, 0, f, F0[f]);
-        }
-        MX_FENCE();
-      });
+      window(std::integral_constant<int, 1>{}, nxs_c, mask_c, dma_c, nst, mk1, pend);
     };
 
-    auto run = [&](auto nxs_c) __attribute__((always_inline)) {
+    // DMA_C: this is a loading wave (waves 0..3, one per SIMD); waves 4..7
+    // issue no DMA and only read LDS and run MFMAs
+    auto run = [&](auto nxs_c, auto dma_c) __attribute__((always_inline)) {
       constexpr int NXS = decltype(nxs_c)::value;
-      {
+      if constexpr (decltype(dma_c)::value) {
         const StageDma d0 = make_stage_dma(smem, 0, L, k0, 0, ns, wv);
         issue_loads<0, 17>(d0, L, wv, lane);
         const StageDma d1 = make_stage_dma(smem, 1, L, k0, 1, ns, wv);
         issue_loads<0, 17>(d1, L, wv, lane);
       }
       asm volatile("s_waitcnt vmcnt(17) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stage 0 has landed
-      static_for<0, 8>([&](auto fc) {
+      if constexpr (NXS > 0) {
+        read(smem, 0, false, 0, FY[0][0]);
+        read(smem, 0, false, 1, FY[0][1]);
+      }
+      static_for<0, 4>([&](auto fc) {
         constexpr int f = decltype(fc)::value;
-        if constexpr (f < 4 ? f < NXS : NXS > 0) read(smem, 0, f, F0[f]);
+        if constexpr (f < NXS) read(smem, 0, true, f, FX[f < 3 ? f : 3]);
       });
       if (MODE == 1) {
         // only a wgrad tile's first and last stage can hold blocks outside
         // its group (stages are whole 128-byte lines of the group's span)
-        stage(nxs_c, std::true_type{}, 0);
-        for (int kt = 1; kt < ns - 1; ++kt) stage(nxs_c, std::false_type{}, kt);
-        if (ns > 1) stage(nxs_c, std::true_type{}, ns - 1);
+        stage(nxs_c, std::true_type{}, dma_c, 0);
+        for (int kt = 1; kt < ns - 1; ++kt) stage(nxs_c, std::false_type{}, dma_c, kt);
+        if (ns > 1) stage(nxs_c, std::true_type{}, dma_c, ns - 1);
       } else {
-        for (int kt = 0; kt < ns; ++kt) stage(nxs_c, std::false_type{}, kt);
+        for (int kt = 0; kt < ns; ++kt) stage(nxs_c, std::false_type{}, dma_c, kt);
       }
     };
     // X sub-tiles of this wave inside the tile (mode 1 tiles are whole in X)
@@ -558,17 +567,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
     using I4 = std::integral_constant<int, 4>;
-    if (MODE == 1 || nxs >= 4) run(I4{});
-    else if (nxs == 3) run(I3{});
-    else if (nxs == 2) run(I2{});
-    else if (nxs == 1) run(I1{});
-    else run(I0{});
+    auto by_nxs = [&](auto dma_c) __attribute__((always_inline)) {
+      if (MODE == 1 || nxs >= 4) run(I4{}, dma_c);
+      else if (nxs == 3) run(I3{}, dma_c);
+      else if (nxs == 2) run(I2{}, dma_c);
+      else if (nxs == 1) run(I1{}, dma_c);
+      else run(I0{}, dma_c);
+    };
+    if (wv < 4) by_nxs(std::true_type{});
+    else by_nxs(std::false_type{});
     // drain the empty-range loads still in flight before the workgroup ends
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
   // epilogue: lane holds output row i = i0 + iw*128 + qx*32 + l32 and, for
-  // register group g, columns j0 + jw*128 + qy*32 + 8g + 4*half + 0..3.
+  // register group g, columns j0 + jw*64 + qy*32 + 8g + 4*half + 0..3.
   const int64_t c_off = MODE == 1 ? (int64_t)e * a.c_estride : 0;
   const int64_t i_lim = x_end;
   if (OUT_F32) {
@@ -579,10 +592,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
       const int64_t dst = a.row_map ? (int64_t)a.row_map[i] : i;
       if (dst < 0 || dst >= a.c_rows) continue;
 #pragma unroll
-      for (int qy = 0; qy < 4; ++qy) {
+      for (int qy = 0; qy < 2; ++qy) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int64_t j = j0 + jw * 128 + qy * 32 + 8 * g + 4 * half;
+          const int64_t j = j0 + jw * 64 + qy * 32 + 8 * g + 4 * half;
           if (j < a.J) {
             const v16f& v = acc[qy][qx];
             float* crow = (float*)a.C + c_off + dst * a.ldc;
@@ -604,7 +617,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
     for (int qx = 0; qx < 4; ++qx) {
       const int row = iw * 128 + qx * 32 + l32;
 #pragma unroll
-      for (int qy = 0; qy < 4; ++qy) {
+      for (int qy = 0; qy < 2; ++qy) {
         const v16f& v = acc[qy][qx];
         // register group g holds columns 8g + 4*half + 0..3.  Trading groups
         // with the partner lane l ^ 32 (group 0 of the upper half for group 1
@@ -623,22 +636,22 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
           const auto x = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
           const auto y = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
           const v4i w = {(int)x[0], (int)y[0], (int)x[1], (int)y[1]};
-          const int col = jw * 128 + qy * 32 + 16 * pr + 8 * half;
+          const int col = jw * 64 + qy * 32 + 16 * pr + 8 * half;
           *(v4i*)(ot + row * kOutPitch + col * 2) = w;
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     __syncthreads();
-    // thread t: 16 bytes (8 columns) of row 8*it + t/32; the J % 8 == 0
+    // thread t: 16 bytes (8 columns) of row 16*it + t/32; the J % 8 == 0
     // contract makes an 8-column group wholly valid or wholly past J.
     // Streaming (nontemporal) stores: the output is not read back here and
     // should not evict the operand rows the other workgroups share in L2.
     const int c8 = (tid & 31) * 8;
     const int64_t j = j0 + c8;
 #pragma unroll 4
-    for (int it = 0; it < kBM / 8; ++it) {
-      const int row = it * 8 + (tid >> 5);
+    for (int it = 0; it < kBM / 16; ++it) {
+      const int row = it * 16 + (tid >> 5);
       const int64_t i = i0 + row;
       const v4i w = *(const v4i*)(ot + row * kOutPitch + c8 * 2);
       // with a row map (routed tokens) the row goes back to its token's place
