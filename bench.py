@@ -281,15 +281,15 @@ def quant_sweep(torch, mx, timer, inp, dev, reps, W, wq):
           torch.empty((Rq // 128, C, 4), dtype=torch.uint8, device=dev))
     res = {}
     for name, kernel, fn, nbytes in (
-            ("weights_both_orientations_16x8192x5120", "mxk::quant_dual_kernel",
+            ("weights_both_orientations_16x8192x5120", "mxk::quant_dual256_kernel<true>",
              lambda: mx.mx_quantize_weights(W, *wq), E * N * K * 4 + 2 * E * N * K // 32),
             ("rowwise_65600x5120", "mxk::quant_rowwise_kernel",
              lambda: mx.mx_quantize_rowwise(X, q, s_row), 3 * R * C + R * C // 32),
-            ("colwise_65600x5120", "mxk::quant_colwise_kernel",
+            ("colwise_65600x5120", "mxk::quant_dual256_kernel<false>",
              lambda: mx.mx_quantize_colwise(X, qt, s_col), 3 * R * C + R * C // 32),
             ("32x32_65600x5120", "mxk::quant_32x32_kernel",
              lambda: mx.mx_quantize_32x32(X, q, s_sq), 3 * R * C + R * C // 1024),
-            ("dual_rowwise_and_colwise_65600x5120", "mxk::quant_dual_kernel",
+            ("dual_rowwise_and_colwise_65600x5120", "mxk::quant_dual256_kernel<true>",
              lambda: mx.mx_quantize_dual(X, Rq, *dq), 4 * R * C + 2 * R * C // 32)):
         fn()
         torch.cuda.synchronize()
