@@ -197,8 +197,23 @@ class Timer:
             e.record()
             torch.cuda.synchronize()
             ts.append(s.elapsed_time(e))
-        ts.sort()
-        return {"mean_ms": sum(ts) / len(ts), "median_ms": ts[len(ts) // 2], "min_ms": ts[0], "max_ms": ts[-1]}
+        return self._stats(ts)
+
+    def time_pair(self, fa, fb, reps, flush=False):
+        """Two functions timed in alternating reps, so both see the same clock
+        and cache state (a variant against its baseline)."""
+        ta = self.time(fa, 1, flush)["all_ms"]
+        tb = self.time(fb, 1, flush)["all_ms"]
+        for _ in range(reps - 1):
+            ta += self.time(fa, 1, flush)["all_ms"]
+            tb += self.time(fb, 1, flush)["all_ms"]
+        return self._stats(ta), self._stats(tb)
+
+    @staticmethod
+    def _stats(ts):
+        ts = sorted(ts)
+        return {"mean_ms": sum(ts) / len(ts), "median_ms": ts[len(ts) // 2], "min_ms": ts[0], "max_ms": ts[-1],
+                "all_ms": ts}
 
 
 def traffic_for_current_kernel():
@@ -571,11 +586,14 @@ def main():
         same = (torch.equal(out_t.view(torch.int16), out[torch.from_numpy(grouped_row).to(dev)].view(torch.int16))
                 and torch.equal(dx_t.view(torch.int16), dA[torch.from_numpy(grouped_row).to(dev)].view(torch.int16)))
         assert int(r_status.item()) == 0
-        t = timer.time(routed, max(3, args.steps // 2), flush=False)
+        # reps alternate with the grouped step, so the two see the same clock
+        t, tg = timer.time_pair(routed, step, max(4, args.steps // 2), flush=False)
         variants["routed_from_token_order"] = {
             "ms": t["median_ms"], "tflops_real_tokens": flops_step_real / (t["median_ms"] * 1e-3) / 1e12,
+            "grouped_step_ms_alternating": tg["median_ms"],
             "rows_capacity": cap, "outputs_bit_identical_to_grouped_step": bool(same)}
-        log(f"routed step {t['median_ms']:.3f} ms (outputs identical to the grouped step: {same})")
+        log(f"routed step {t['median_ms']:.3f} ms against {tg['median_ms']:.3f} ms for the grouped step in "
+            f"alternating reps (outputs identical to the grouped step: {same})")
         del x_tok, g_tok, ra, rg, out_t, dx_t
 
         # the same step through the three all-bf16 entry points (W quantized twice)
