@@ -70,21 +70,48 @@ def test_every_gemm_kernel_fits_two_waves_per_simd(gemm_asm):
     assert "grouped_gemm_kernel" in text
 
 
+def _loop_blocks(lines):
+    """Basic blocks of the GEMM kernels as (kernel, loop headers enclosing the
+    block, block lines), from the compiler's loop annotations ("Loop Header",
+    "in Loop: Header=", "Parent Loop") on each block label."""
+    blocks, cur = [], None
+    kern = None
+    for i, l in enumerate(lines):
+        m = re.match(r"^(_ZN3mxk19grouped_gemm_kernel\S*):", l)
+        if m:
+            kern, cur = m.group(1), None
+            continue
+        if kern is None:
+            continue
+        if l.startswith(".Lfunc_end"):
+            kern, cur = None, None
+            continue
+        m = re.match(r"^(\.LBB(\d+_\d+)|; %bb\.\d+):(.*)$", l)
+        if m:
+            ann, j = m.group(3), i + 1
+            while j < len(lines) and re.match(r"^\s+;", lines[j]):
+                ann += " " + lines[j]
+                j += 1
+            loops = set(re.findall(r"(?:Header=|Parent Loop )BB(\d+_\d+)", ann))
+            if "Loop Header" in ann and m.group(2):
+                loops.add(m.group(2))
+            cur = (kern, loops, [])
+            blocks.append(cur)
+        elif cur is not None:
+            cur[2].append(l)
+    return blocks
+
+
 def test_no_stage_loop_spills(gemm_asm):
-    offenders = []
-    for name, (lo, hi) in _kernels(gemm_asm).items():
-        body = gemm_asm[lo:hi]
-        heads = [(i, m.group(1)) for i, l in enumerate(body)
-                 if (m := re.match(r"^(\.LBB\d+_\d+):.*Loop Header", l))]
-        assert heads, name
-        for start, lab in heads:
-            back = [j for j in range(start + 1, len(body))
-                    if re.search(r"s_(c)?branch\w*\s+%s$" % re.escape(lab), body[j])]
-            if not back:
-                continue
-            seg = body[start:back[-1] + 1]
-            mfma = sum("v_mfma" in x for x in seg)
-            scratch = sum("scratch_" in x for x in seg)
-            if mfma and scratch:
-                offenders.append((name, lab, mfma, scratch))
+    """No loop that issues MFMAs (counting every block the compiler places in
+    it, nested loops included) holds a scratch access."""
+    per_loop = {}
+    for kern, loops, body in _loop_blocks(gemm_asm):
+        mfma = sum("v_mfma" in x for x in body)
+        scratch = sum("scratch_" in x for x in body)
+        for h in loops:
+            m, s = per_loop.get((kern, h), (0, 0))
+            per_loop[(kern, h)] = (m + mfma, s + scratch)
+    assert per_loop, "no loops found"
+    offenders = {k: v for k, v in per_loop.items() if v[0] and v[1]}
     assert not offenders, offenders
