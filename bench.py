@@ -56,6 +56,7 @@ PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, published
 GEMM_KERNEL = "mxk::grouped_gemm_kernel<0, false>"
 GEMM_SOURCE = os.path.join(ROOT, "mxfp8_block_scaled_06_amd", "csrc", "mx_gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fwd_llama4_traffic.json")
+WARMUP_LAUNCHES = 5          # untimed launches before each per-kernel figure
 FLUSH_BYTES = 1 << 30
 MICRO_BATCHES = 4
 
@@ -69,7 +70,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--reps", type=int, default=10, help="timed launches per GEMM-only / quantize figure")
+    p.add_argument("--reps", type=int, default=20, help="timed launches per GEMM-only / quantize figure")
     p.add_argument("--quick", action="store_true",
                    help="only the timed Llama4 step and the roofline of its forward GEMM launches (no GEMM-only "
                         "figures, step variants, quantize sweep, other workloads or CPU leg): the launches a "
@@ -265,7 +266,8 @@ def gemm_only(torch, mx, timer, x, dev, reps, ops, tag):
     res = {"E": E, "rows": M, "tokens": T, "K": K, "N": N,
            "counts_min_max": [int(x.counts.min()), int(x.counts.max())]}
     for op in ops:
-        fns[op]()
+        for _ in range(WARMUP_LAUNCHES):
+            fns[op]()
         torch.cuda.synchronize()
         t = timer.time(fns[op], reps)
         res[op] = gemm_entry(t, 2.0 * T * N * K, 2.0 * M * N * K)
@@ -306,7 +308,8 @@ def quant_sweep(torch, mx, timer, inp, dev, reps, W, wq):
              lambda: mx.mx_quantize_32x32(X, q, s_sq), 3 * R * C + R * C // 1024),
             ("dual_rowwise_and_colwise_65600x5120", "mxk::quant_dual256_kernel<true>",
              lambda: mx.mx_quantize_dual(X, Rq, *dq), 4 * R * C + 2 * R * C // 32)):
-        fn()
+        for _ in range(WARMUP_LAUNCHES):
+            fn()
         torch.cuda.synchronize()
         t = timer.time(fn, reps)
         gbs = nbytes / (t["median_ms"] * 1e-3) / 1e9
@@ -686,8 +689,8 @@ def main():
         "cpu_baseline": cpu,
         "vendor_reference": vendor,
         "timing": "step and step variants: HIP events around back-to-back steps (caches as the previous step "
-                  "leaves them); GEMM-only and quantize figures: median of per-launch HIP events, each launch after "
-                  "an untimed 1 GiB write",
+                  f"leaves them); GEMM-only and quantize figures: {WARMUP_LAUNCHES} untimed launches, then the median "
+                  f"of {args.reps} per-launch HIP events, each launch after an untimed 1 GiB write",
         "inputs_sha256": digests,
         "host": host_info(),
         "gpu": torch.cuda.get_device_name(0),
