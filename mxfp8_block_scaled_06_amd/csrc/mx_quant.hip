@@ -98,16 +98,23 @@ __global__ __launch_bounds__(kRowThreads) void quant_rowwise_gather_kernel(const
                                                                            uint32_t chunks_per_row,
                                                                            uint32_t out_rows) {
   const int64_t base = (int64_t)blockIdx.x * (kRowThreads * kRowU) + threadIdx.x;
+  // the row indices of all kRowU chunks first, then the data: no data load
+  // waits behind an index load
+  int sr[kRowU];
+#pragma unroll
+  for (int u = 0; u < kRowU; ++u) {
+    const int64_t idx = min(base + (int64_t)u * kRowThreads, nchunks - 1);   // nchunks > 0: the grid is empty otherwise
+    sr[u] = rows[(uint32_t)(idx / chunks_per_row)];
+  }
   v4i w[kRowU];
 #pragma unroll
   for (int u = 0; u < kRowU; ++u) {
     const int64_t idx = base + (int64_t)u * kRowThreads;
     w[u] = (v4i){0, 0, 0, 0};
-    if (idx < nchunks) {
+    if (idx < nchunks && sr[u] >= 0 && sr[u] < src_rows) {
       const uint32_t r = (uint32_t)(idx / chunks_per_row);
       const uint32_t c = (uint32_t)(idx - (int64_t)r * chunks_per_row);
-      const int64_t sr = rows[r];
-      if (sr >= 0 && sr < src_rows) w[u] = __builtin_nontemporal_load((const v4i*)(x + sr * cols + c * 8));
+      w[u] = __builtin_nontemporal_load((const v4i*)(x + (int64_t)sr[u] * cols + c * 8));
     }
   }
 #pragma unroll
@@ -269,20 +276,32 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
   const int64_t n0 = (int64_t)blockIdx.y * kColTile;   // ldq % 128 == 0: rows [N, ldq) read as zeros
   const int64_t k0 = (int64_t)blockIdx.x * kColTile;
   const uint16_t* wb = w + b * N * K;
+  // input row of each of the thread's 8 chunks (-1: a zero row).  Gathered
+  // rows: row n of the tile is input row rows[n] / topk (negative or out of
+  // range: a zero row, the padding of an expert group); the row indices are
+  // all loaded before any data.
+  int64_t src[8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int64_t n = n0 + ((it * 256 + tid) >> 4);
+    src[it] = n < N ? n : -1;
+  }
+  if (rows != nullptr && N > 0) {
+    int idx[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) idx[it] = rows[min(n0 + ((it * 256 + tid) >> 4), N - 1)];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int64_t item = src[it] >= 0 ? (int64_t)idx[it] : -1;
+      src[it] = item >= 0 && item < n_items ? (topk == 1 ? item : (int64_t)((uint32_t)item / topk)) : -1;
+    }
+  }
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
     const int chunk = it * 256 + tid;
     const int rr = chunk >> 4, cc = chunk & 15;
     v4i v = (v4i){0, 0, 0, 0};
-    if (n0 + rr < N) {
-      // gathered rows: row n of the tile is input row rows[n] / topk
-      // (negative or out of range: a zero row, the padding of an expert group)
-      const int64_t item = rows ? (int64_t)rows[n0 + rr] : n0 + rr;
-      if (item >= 0 && item < n_items) {
-        const int64_t src = topk == 1 ? item : (int64_t)((uint32_t)item / topk);
-        v = __builtin_nontemporal_load((const v4i*)(wb + src * K + k0 + cc * 8));
-      }
-    }
+    if (src[it] >= 0) v = __builtin_nontemporal_load((const v4i*)(wb + src[it] * K + k0 + cc * 8));
     *(v4i*)(tile + rr * kDualPitch + cc * 16) = v;
   }
   __syncthreads();
@@ -414,20 +433,29 @@ __global__ __launch_bounds__(kD2Threads) __attribute__((amdgpu_waves_per_eu(4)))
   const uint16_t* wb = w + b * N * K;
   const int r0 = 32 * wv + 16 * half;          // tile row of this lane's i = 0
 
+  // input row of each of the lane's 16 rows (-1: a zero row).  Gathered
+  // rows: row n is input row rows[n] / topk (negative or out of range: a zero
+  // row, the padding of an expert group).  All 16 row indices are loaded
+  // before any data, so no data load waits behind an index load.
+  int64_t src[16];
+  if (rows != nullptr && N > 0) {
+    int idx[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) idx[i] = rows[min(n0 + r0 + i, N - 1)];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t item = n0 + r0 + i < N ? (int64_t)idx[i] : -1;
+      src[i] = item >= 0 && item < n_items ? (topk == 1 ? item : (int64_t)((uint32_t)item / topk)) : -1;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) src[i] = rows == nullptr && n0 + r0 + i < N ? n0 + r0 + i : -1;
+  }
   v4i v[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int64_t n = n0 + r0 + i;
     v4i x = (v4i){0, 0, 0, 0};
-    if (n < N) {
-      // gathered rows: row n is input row rows[n] / topk (negative or out of
-      // range: a zero row, the padding of an expert group)
-      const int64_t item = rows ? (int64_t)rows[n] : n;
-      if (item >= 0 && item < n_items) {
-        const int64_t src = topk == 1 ? item : (int64_t)((uint32_t)item / topk);
-        x = __builtin_nontemporal_load((const v4i*)(wb + src * K + k0 + 8 * pc));
-      }
-    }
+    if (src[i] >= 0) x = __builtin_nontemporal_load((const v4i*)(wb + src[i] * K + k0 + 8 * pc));
     v[i] = x;
   }
 
