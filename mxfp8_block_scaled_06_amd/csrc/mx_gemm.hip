@@ -585,11 +585,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
   const int64_t c_off = MODE == 1 ? (int64_t)e * a.c_estride : 0;
   const int64_t i_lim = x_end;
   if (OUT_F32) {
+    // destination rows first: a load issued after a store waits for it
+    int64_t dsts[4];
 #pragma unroll
     for (int qx = 0; qx < 4; ++qx) {
       const int64_t i = i0 + iw * 128 + qx * 32 + l32;
-      if (i >= i_lim) continue;
-      const int64_t dst = a.row_map ? (int64_t)a.row_map[i] : i;
+      dsts[qx] = i >= i_lim ? -1 : (a.row_map ? (int64_t)a.row_map[i] : i);
+    }
+#pragma unroll
+    for (int qx = 0; qx < 4; ++qx) {
+      const int64_t dst = dsts[qx];
       if (dst < 0 || dst >= a.c_rows) continue;
 #pragma unroll
       for (int qy = 0; qy < 2; ++qy) {
@@ -649,13 +654,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
     // should not evict the operand rows the other workgroups share in L2.
     const int c8 = (tid & 31) * 8;
     const int64_t j = j0 + c8;
+    // with a row map (routed tokens) each row goes back to its token's place;
+    // the thread's 16 map entries are loaded before any store, since a load
+    // issued after a store waits for it (one counter for both)
+    int rmv[kBM / 16];
+#pragma unroll
+    for (int it = 0; it < kBM / 16; ++it) {
+      const int64_t i = i0 + it * 16 + (tid >> 5);
+      rmv[it] = a.row_map != nullptr && i < i_lim ? a.row_map[i] : -1;
+    }
 #pragma unroll 4
     for (int it = 0; it < kBM / 16; ++it) {
       const int row = it * 16 + (tid >> 5);
       const int64_t i = i0 + row;
       const v4i w = *(const v4i*)(ot + row * kOutPitch + c8 * 2);
-      // with a row map (routed tokens) the row goes back to its token's place
-      const int64_t dst = i < i_lim ? (a.row_map ? (int64_t)a.row_map[i] : i) : -1;
+      const int64_t dst = i < i_lim ? (a.row_map ? (int64_t)rmv[it] : i) : -1;
       if (dst >= 0 && dst < a.c_rows && j < a.J)
         __builtin_nontemporal_store(w, (v4i*)((uint16_t*)a.C + c_off + dst * a.ldc + j));
     }
