@@ -235,14 +235,39 @@ __global__ __launch_bounds__(256) void topk_sum_kernel(const float* __restrict__
   if (idx >= T * per_row) return;
   const int64_t t = idx / per_row, c = (idx - t * per_row) * 8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const v4i* src = (const v4i*)(x + (t * k + j) * cols + c);
-    const v4i a = __builtin_nontemporal_load(src), b = __builtin_nontemporal_load(src + 1);
+  auto add = [&](const v4i& a, const v4i& b) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       acc[u] += __int_as_float(a[u]);
       acc[4 + u] += __int_as_float(b[u]);
     }
+  };
+  // slots four at a time (then two, then one): their loads go out together,
+  // the additions stay in slot order
+  int j = 0;
+  for (; j + 4 <= k; j += 4) {
+    v4i a[4], b[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const v4i* src = (const v4i*)(x + (t * k + j + q) * cols + c);
+      a[q] = __builtin_nontemporal_load(src);
+      b[q] = __builtin_nontemporal_load(src + 1);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) add(a[q], b[q]);
+  }
+  if (j + 2 <= k) {
+    const v4i* s0 = (const v4i*)(x + (t * k + j) * cols + c);
+    const v4i* s1 = (const v4i*)(x + (t * k + j + 1) * cols + c);
+    const v4i a0 = __builtin_nontemporal_load(s0), b0 = __builtin_nontemporal_load(s0 + 1);
+    const v4i a1 = __builtin_nontemporal_load(s1), b1 = __builtin_nontemporal_load(s1 + 1);
+    add(a0, b0);
+    add(a1, b1);
+    j += 2;
+  }
+  if (j < k) {
+    const v4i* src = (const v4i*)(x + (t * k + j) * cols + c);
+    add(__builtin_nontemporal_load(src), __builtin_nontemporal_load(src + 1));
   }
   const v4i o = {(int)pack_bf16x2_rne(acc[0], acc[1]), (int)pack_bf16x2_rne(acc[2], acc[3]),
                  (int)pack_bf16x2_rne(acc[4], acc[5]), (int)pack_bf16x2_rne(acc[6], acc[7])};

@@ -302,7 +302,8 @@ def test_routed_experts_full_size_llama4_sampled():
 # --------------------------------------------------------------------------
 # Top-k routers
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("T,k,cols", [(300, 3, 264), (64, 1, 128), (1000, 8, 512)])
+@pytest.mark.parametrize("T,k,cols", [(300, 3, 264), (64, 1, 128), (1000, 8, 512), (300, 2, 264), (120, 4, 512),
+                                      (200, 5, 128), (150, 6, 136), (100, 7, 256)])
 def test_topk_sum_rows_matches_oracle(T, k, cols):
     torch = require_gpu()
     import mxfp8_block_scaled_06_amd as mx
