@@ -256,7 +256,8 @@ struct LoadState {
   int64_t sx_chunk, sy_chunk;       // bytes between scale chunks (rows x 4)
   int64_t sx_rows4, sy_rows4;       // valid scale bytes per chunk from sxb / syb
   int64_t nchunks;                  // scale chunks per row (Kc / 128)
-  int voff[8];                      // data piece offsets (X and Y share the row stride)
+  int voff[2];                      // data piece offsets of loads u = 0, 1 (X and Y share the row stride)
+  int ldx16;                        // bytes of 16 rows: load u + 2 is 16 rows below load u (same swizzle)
 };
 
 // DMA of one stage (contraction bytes [k0 + 128*stage_no, +128)) into LDS
@@ -295,10 +296,11 @@ __device__ __forceinline__ void issue_load(const StageDma& d, const LoadState& L
   if (n < 16) {
     const int u = n >> 1;
     const int c = wv * 8 + u;   // 1 KiB chunk = 8 rows x 128 B
+    const int vo = L.voff[u & 1] + (u >> 1) * L.ldx16;
     if ((n & 1) == 0) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rx, (lds_void*)(d.st + c * 1024), 16, L.voff[u], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rx, (lds_void*)(d.st + c * 1024), 16, vo, 0, 0, 0);
     } else {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ry, (lds_void*)(d.st + kTileBytes + c * 1024), 16, L.voff[u], 0, 0,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ry, (lds_void*)(d.st + kTileBytes + c * 1024), 16, vo, 0, 0,
                                                0);
     }
   } else {
@@ -416,8 +418,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
   L.sx_rows4 = (a.I - i0) * 4;     // rows past a group end hold a neighbour's (finite) scales
   L.sy_rows4 = (a.J - j0) * 4;
   L.nchunks = a.Kc / kBK;
+  L.ldx16 = 16 * (int)a.ldx;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < 2; ++u) {
     const int row = ((wv & 3) * 8 + u) * 8 + (lane >> 3);
     L.voff[u] = row * (int)a.ldx + (((lane & 7) ^ piece_swz(row)) << 4);
   }
@@ -444,20 +447,23 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
     // A window's MFMAs run X sub-tile by X sub-tile, so FX[qx] is refilled for
     // the next window right after its second MFMA.
     Frag FX[5], FY[2][2];
-    int xo[2][2], yo[2][2];
+    // Y's fragments sit a wave-uniform distance from X's (same lane row and
+    // piece swizzle), so only X's per-lane offsets are held and Y's read
+    // goes through a shifted stage base
+    int xo[2][2];
 #pragma unroll
     for (int w = 0; w < 2; ++w)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        xo[w][c] = xrow0 * kBK + pc[w][c];
-        yo[w][c] = kTileBytes + yrow0 * kBK + pc[w][c];
-      }
-    const int sxo = 2 * kTileBytes + xrow0 * 4 + half, syo = 2 * kTileBytes + 2 * kScaleChunk + yrow0 * 4 + half;
+      for (int c = 0; c < 2; ++c) xo[w][c] = xrow0 * kBK + pc[w][c];
+    const int sxo = 2 * kTileBytes + xrow0 * 4 + half;
+    const int ydelta = uni32(kTileBytes + (yrow0 - xrow0) * kBK);
+    const int sdelta = uni32(2 * kScaleChunk + (yrow0 - xrow0) * 4);
     // sub-tile `sub` of operand X (isx) or Y, window `w`, stage buffer `st`
     auto read = [&](const uint8_t* st, int w, bool isx, int sub, Frag& dst) {
-      const uint8_t* p0 = st + (isx ? xo[w][0] : yo[w][0]) + sub * 32 * kBK;
-      const uint8_t* p1 = st + (isx ? xo[w][1] : yo[w][1]) + sub * 32 * kBK;
-      const uint8_t* ps = st + (isx ? sxo : syo) + sub * 32 * 4 + 2 * w;
+      const uint8_t* sb = st + (isx ? 0 : ydelta);
+      const uint8_t* p0 = sb + xo[w][0] + sub * 32 * kBK;
+      const uint8_t* p1 = sb + xo[w][1] + sub * 32 * kBK;
+      const uint8_t* ps = st + (isx ? 0 : sdelta) + sxo + sub * 32 * 4 + 2 * w;
       const v4i a0 = *(const v4i*)p0;
       const v4i a1 = *(const v4i*)p1;
       dst.s = *ps;
