@@ -49,6 +49,7 @@ MODES = ["rowwise", "colwise", "32x32"]
     ((32, 32), 5, 1.0),             # a single block / tile
     ((224, 200), 6, 1.0),           # ragged column count (not a tile multiple)
     ((2, 288, 512), 7, 0.02),       # batched, 256-column tiles with a partial last row tile
+    ((3, 992, 768), 8, 1.0),        # 36 tiles of 256 x 256: tile chunks crossing batches and slot groups
 ])
 def test_quant_seeded(mode, shape, seed, std):
     require_gpu()
