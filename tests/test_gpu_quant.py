@@ -50,6 +50,7 @@ MODES = ["rowwise", "colwise", "32x32"]
     ((224, 200), 6, 1.0),           # ragged column count (not a tile multiple)
     ((2, 288, 512), 7, 0.02),       # batched, 256-column tiles with a partial last row tile
     ((3, 992, 768), 8, 1.0),        # 36 tiles of 256 x 256: tile chunks crossing batches and slot groups
+    ((2, 512, 2048), 9, 1.0),       # 32 tiles, aligned rows: the plain tile order over batches
 ])
 def test_quant_seeded(mode, shape, seed, std):
     require_gpu()
