@@ -418,16 +418,16 @@ __device__ __forceinline__ int d2_slot(int k, int slot) { return slot ^ ((k >> 3
 // scales go to the GEMM layout when st_ld == 0, else row-major [batch][K][st_ld]
 // (blocks n0/32 .. of row k).  128 VGPRs: two workgroups per CU.
 //
-// Tile order.  The dual pass takes a 3D grid, column tiles fastest.  The
-// colwise pass takes a 1D grid of slots (slot s runs on XCD s % 8), and
-// slot s is tile s, column tiles fastest, unless both
+// Tile order.  Both passes take a 3D grid, column tiles fastest, except the
+// colwise pass when both
 //  * ldq % 128 != 0: the transposed rows start off a 128-byte line, so
 //    row-tile neighbours write the two halves of shared lines, and
 //  * the column-tile count is not a multiple of 8: in that order row-tile
 //    neighbours then run on different XCDs, whose L2s write their halves
 //    of each shared line separately.
-// Then each XCD walks chunks of kColChunk row tiles of one column tile, row
-// tiles fastest, so one L2 merges the halves close together in time: +9% on
+// Then it takes a 1D grid of slots (slot s runs on XCD s % 8) in which each
+// XCD walks chunks of kColChunk row tiles of one column tile, row tiles
+// fastest, so one L2 merges the halves close together in time: +9% on
 // [65600, 5120].  The chunks scatter the row reads, which costs 7-11% where
 // there is nothing to merge, hence the two conditions.
 constexpr int kColChunk = 4;
@@ -446,28 +446,17 @@ __global__ __launch_bounds__(kD2Threads) __attribute__((amdgpu_waves_per_eu(4)))
   __shared__ __attribute__((aligned(16))) uint8_t scol[kD2N / 128 * kD2 * 4];   // [n chunk][256 cols][4 blocks]
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, pc = lane & 31;
-  int64_t b, n0, k0;
-  if constexpr (ROWWISE) {
-    b = blockIdx.z;
-    n0 = (int64_t)blockIdx.y * kD2N;
-    k0 = (int64_t)blockIdx.x * kD2;
-  } else {
-    const int64_t tx = K / kD2, ty = (ldq + kD2N - 1) / kD2N;
-    const int64_t sl = blockIdx.x;
-    if (!col_chunked(K, ldq)) {
-      b = sl / (tx * ty);
-      const int64_t r = sl - b * tx * ty;
-      n0 = (r / tx) * kD2N;
-      k0 = (r % tx) * kD2;
-    } else {
-      const int64_t si = sl >> 3;
-      const int64_t t = ((si / kColChunk) * 8 + (sl & 7)) * kColChunk + si % kColChunk;
-      if (t >= tx * ty * batches) return;     // padding slot (uniform over the workgroup)
-      b = t / (tx * ty);
-      const int64_t r = t - b * tx * ty;
-      n0 = (r % ty) * kD2N;
-      k0 = (r / ty) * kD2;
-    }
+  int64_t b = blockIdx.z, n0 = (int64_t)blockIdx.y * kD2N, k0 = (int64_t)blockIdx.x * kD2;
+  if (!ROWWISE && col_chunked(K, ldq)) {
+    // 1D grid of slots; 32-bit arithmetic (the launcher bounds the slot count)
+    const uint32_t tx = (uint32_t)(K / kD2), ty = (uint32_t)((ldq + kD2N - 1) / kD2N);
+    const uint32_t sl = blockIdx.x, si = sl >> 3;
+    const uint32_t t = ((si / kColChunk) * 8 + (sl & 7)) * kColChunk + si % kColChunk;
+    if (t >= tx * ty * (uint32_t)batches) return;     // padding slot (uniform over the workgroup)
+    const uint32_t bt = t / (tx * ty), r = t - bt * tx * ty;
+    b = bt;
+    n0 = (int64_t)(r % ty) * kD2N;
+    k0 = (int64_t)(r / ty) * kD2;
   }
   const uint16_t* wb = w + b * N * K;
   const int r0 = 32 * wv + 16 * half;          // tile row of this lane's i = 0
@@ -677,11 +666,15 @@ hipError_t launch_quant_colwise(const uint16_t* x, int64_t batch, int64_t rows, 
   if (batch == 0 || rows == 0 || cols == 0) return hipSuccess;
   if (cols % kD2 == 0 && (gemm_layout ? ldq % 128 == 0 : ldq == rows)) {
     // codes of rows [rows, ldq) are zero codes (ldq rounded up to the tile)
-    const int64_t tiles = (cols / kD2) * ((ldq + kD2N - 1) / kD2N) * batch;
-    const int64_t slots =
-        col_chunked(cols, ldq) ? (tiles + 8 * kColChunk - 1) / (8 * kColChunk) * (8 * kColChunk) : tiles;
-    hipLaunchKernelGGL(quant_dual256_kernel<false>, dim3((unsigned)slots), dim3(kD2Threads), 0, st, x, rows, cols,
-                       ldq, (uint8_t*)nullptr, (uint8_t*)nullptr, q_t, s_t, gemm_layout ? (int64_t)0 : lds,
+    const int64_t tx = cols / kD2, ty = (ldq + kD2N - 1) / kD2N;
+    dim3 grid((unsigned)tx, (unsigned)ty, (unsigned)batch);
+    if (col_chunked(cols, ldq)) {
+      const int64_t slots = (tx * ty * batch + 8 * kColChunk - 1) / (8 * kColChunk) * (8 * kColChunk);
+      if (slots > (int64_t)UINT32_MAX / 2) return hipErrorInvalidValue;
+      grid = dim3((unsigned)slots);
+    }
+    hipLaunchKernelGGL(quant_dual256_kernel<false>, grid, dim3(kD2Threads), 0, st, x, rows, cols, ldq,
+                       (uint8_t*)nullptr, (uint8_t*)nullptr, q_t, s_t, gemm_layout ? (int64_t)0 : lds,
                        (const int32_t*)nullptr, rows, 1u, batch);
     return hipGetLastError();
   }
