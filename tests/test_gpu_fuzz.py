@@ -158,3 +158,48 @@ def test_wgrad_random_groups(case):
             assert (got[e] == 0).all(), f"empty expert {e} must get exact zeros"
     _check(got, oracle.grouped_mm_wgrad(G, A, offs), oracle.grouped_mm_wgrad(G, A, offs, absolute=True),
            f"wgrad case {case}")
+
+
+@pytest.mark.parametrize("case", range(N_GEMM))
+def test_routed_experts_random_routings(case):
+    """mx_routed_experts forward and backward over random routings: top-1 to
+    top-3, skewed expert loads with empty experts, and (with check=False)
+    some ids outside [0, E), whose items must come out as zero rows."""
+    torch = require_gpu()
+    import mxfp8_block_scaled_06_amd as mx
+    from mxfp8_block_scaled_06_amd.autograd import WeightCache
+    rng = np.random.default_rng(9950 + case)
+    T, E, k = int(rng.integers(1, 500)), int(rng.integers(1, 12)), int(rng.integers(1, 4))
+    K, N = 128 * int(rng.integers(1, 4)), 128 * int(rng.integers(1, 4))
+    p = rng.dirichlet(np.full(E, 0.5))
+    ids = rng.choice(E, size=(T, k), p=p).astype(np.int32)
+    drop = case % 3 == 2
+    if drop:
+        ids[rng.random((T, k)) < 0.05] = E
+    x = inp.random_bf16((T, K), seed=int(rng.integers(1 << 30)), outliers=True)
+    W = inp.random_bf16((E, N, K), seed=int(rng.integers(1 << 30)), std=0.02)
+    G = inp.random_bf16((T * k, N), seed=int(rng.integers(1 << 30)), std=1e-3)
+    log(f"fuzz routed case={case} T={T} E={E} k={k} K={K} N={N} drop={drop} "
+        f"loads={np.bincount(ids.ravel(), minlength=E + 1).tolist()}")
+    xd = to_dev_bf16(x).requires_grad_(True)
+    Wd = to_dev_bf16(W).requires_grad_(True)
+    ids_d = to_dev_i32(ids if k > 1 else ids[:, 0])
+    out = mx.mx_routed_experts(xd, ids_d, Wd, cache=WeightCache(), check=not drop)
+    out.backward(to_dev_bf16(G).view(out.shape))
+    torch.cuda.synchronize()
+    flat = ids.reshape(-1)
+    cap = mx.route_capacity(T * k, E)
+    got_out = bf16_host_bits(out).reshape(T * k, N)
+    if drop:
+        assert (got_out[flat == E] == 0).all()
+    for name, got, ref, absr in (
+            ("out", got_out, oracle.routed_fwd(x, flat, W, cap, topk=k),
+             oracle.routed_fwd(x, flat, W, cap, absolute=True, topk=k)),
+            ("dx", bf16_host_bits(xd.grad), oracle.routed_dgrad(G, flat, W, cap, topk=k),
+             oracle.routed_dgrad(G, flat, W, cap, absolute=True, topk=k)),
+            ("dW", bf16_host_bits(Wd.grad), oracle.routed_wgrad(G, x, flat, E, cap, topk=k),
+             oracle.routed_wgrad(G, x, flat, E, cap, absolute=True, topk=k))):
+        _check(got, ref, absr, f"routed case {case} {name}")
+    for e in range(E):
+        if not (flat == e).any():
+            assert (bf16_host_bits(Wd.grad)[e] == 0).all(), f"expert {e} has no items: dW must be zeros"
